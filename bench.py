@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the TwoTower denoiser hot path on MI355X.
+
+Workload: the full denoise loop for one 16-token block -- B=32 sequences,
+6 attention layers with independent paged bf16 context caches (H_q=32,
+H_kv=2, D=128, 256-token pages, lengths uniform over multiples of 16 in
+[2048, 8192]), T=4 denoise steps, each step = 6 x tt_block_attn + 1 x tt_unmask
+on fp32 logits [512, 131072] committing ceil(masked / remaining) slots per
+sequence, then 6 x tt_kv_append (block commit).
+
+One bench step = one block = 4 denoise steps + the commit; the block's state
+(ctx_lens, mask) is reset from a saved copy at the start of each block so
+every block runs the same workload.  value = denoise steps per second for the
+whole batch.  Inputs are resident in HBM before timing; the 1 GiB of per-step
+logits and ~1.1 GB of caches exceed the 256 MB Infinity Cache, so the loop
+streams from HBM.
+
+The dominant kernel (block attention) is timed again on its own with HIP
+events (rotating over the 24 (step, layer) inputs) for the roofline entry;
+the CPU oracle is timed on a bounded sample for the cpu_baseline entry.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("block-attn HBM GB/s & TFLOP/s (fraction of peak); denoise-steps/sec, 1 GPU")
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_split_config5_counters.md")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "tt_internal.h"):
+        with open(os.path.join(ROOT, "two_tower_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    rec = None
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if line.startswith("COUNTERS_JSON "):
+                rec = json.loads(line[len("COUNTERS_JSON "):])
+    if not rec or rec.get("source_hash") != attn_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed blocks (4 denoise steps each)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-iters", type=int, default=96, help="launches in the attention-only timing")
+    ap.add_argument("--only-attn", action="store_true", help="profiling aid: attention launches only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import two_tower_attention_amd as tt
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not os.path.exists(tt.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    tt.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    lp = workloads.config5(extra_blocks=1)
+    B, S, T, NL, V = lp.B, lp.S, lp.steps, lp.layers, lp.vocab
+    log("generated inputs in %.1fs" % (time.perf_counter() - t_gen))
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    p0 = lp.pools[0]
+    desc = tt.make_desc(B, S, lp.Hq, lp.Hkv, lp.D, lp.page_size, p0.page_table.shape[1],
+                        p0.k_pages.shape[0], int(p0.ctx_lens.max()))
+    kp = [dev_bf16(p.k_pages) for p in lp.pools]
+    vp = [dev_bf16(p.v_pages) for p in lp.pools]
+    pt = [dev_t(p.page_table) for p in lp.pools]
+    ctx0 = torch.stack([dev_t(p.ctx_lens) for p in lp.pools])       # [NL, B] saved lengths
+    ctx = ctx0.clone()
+    q = [[dev_bf16(lp.q[s][i]) for i in range(NL)] for s in range(T)]
+    kb = [[dev_bf16(lp.k_blk[s][i]) for i in range(NL)] for s in range(T)]
+    vb = [[dev_bf16(lp.v_blk[s][i]) for i in range(NL)] for s in range(T)]
+    logits = [dev_t(l) for l in lp.logits]
+    ones = torch.ones((B, S), dtype=torch.uint8, device=dev)
+    mask = ones.clone()
+    out = [torch.empty((B, S, lp.Hq, lp.D), dtype=torch.bfloat16, device=dev) for _ in range(NL)]
+    ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+    com = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(tt.tt_block_attn_workspace_bytes(desc), 16), dtype=torch.uint8, device=dev)
+    uws = torch.empty(max(tt.tt_unmask_workspace_bytes(B, S, V), 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def attn(s, i, stream=None):
+        tt.tt_block_attn(desc, q[s][i], kb[s][i], vb[s][i], kp[i], vp[i], pt[i], ctx[i], out[i],
+                         ws, stream)
+
+    def one_block():
+        ctx.copy_(ctx0)
+        mask.copy_(ones)
+        for s in range(T):
+            for i in range(NL):
+                attn(s, i)
+            tt.tt_unmask(logits[s], mask, None, T - s, ids, com, None, tt.TT_UNMASK_UPDATE_MASK, uws)
+        for i in range(NL):
+            tt.tt_kv_append(desc, kb[T - 1][i], vb[T - 1][i], kp[i], vp[i], pt[i], ctx[i])
+
+    use_graph = not args.no_graph and not args.only_attn
+    graph = None
+    if not args.only_attn:
+        one_block()                      # eager run first (also warms the library)
+        torch.cuda.synchronize()
+        if use_graph:
+            graph = torch.cuda.CUDAGraph()
+            s_cap = torch.cuda.Stream()
+            s_cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s_cap):
+                with torch.cuda.graph(graph, stream=s_cap):
+                    one_block()
+            torch.cuda.current_stream().wait_stream(s_cap)
+            torch.cuda.synchronize()
+        run = graph.replay if graph is not None else one_block
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_s = e0.elapsed_time(e1) / 1e3
+        log("timed %d blocks: wall %.3f ms, events %.3f ms" % (args.steps, wall * 1e3, ev_s * 1e3))
+        block_s = max(wall, ev_s) / args.steps
+        # the last block must have committed every slot
+        assert int(mask.sum().item()) == 0, "denoise loop left masked slots"
+    else:
+        block_s = float("nan")
+
+    # ---- attention alone, HIP events on the launch stream, rotating inputs
+    stream = torch.cuda.current_stream()
+    ctx.copy_(ctx0)
+    for it in range(6):
+        attn(it % T, it % NL)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for it in range(args.attn_iters):
+        attn((it // NL) % T, it % NL)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    attn_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
+    lens = p0.ctx_lens.astype(np.int64)
+    kv_bytes = int(lens.sum()) * lp.Hkv * lp.D * 2 * 2
+    qo_bytes = 2 * B * S * lp.Hq * lp.D * 2
+    blk_bytes = 2 * B * S * lp.Hkv * lp.D * 2
+    attn_bytes = kv_bytes + qo_bytes + blk_bytes
+    attn_flops = 4 * lp.D * S * lp.Hq * int((lens + S).sum())
+    attn_gbs = attn_bytes / attn_s / 1e9
+    attn_tfs = attn_flops / attn_s / 1e12
+    log("attention: %.1f us/launch, %.0f GB/s, %.0f TFLOP/s" % (attn_s * 1e6, attn_gbs, attn_tfs))
+
+    # ---- unmask alone
+    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_un = 16
+    u0.record(stream)
+    for it in range(n_un):
+        mask.copy_(ones)
+        tt.tt_unmask(logits[it % T], mask, None, 4, ids, com, None, 0, uws)
+    u1.record(stream)
+    torch.cuda.synchronize()
+    un_s = u0.elapsed_time(u1) / 1e3 / n_un
+    un_gbs = B * S * V * 4 / un_s / 1e9
+    log("unmask: %.1f us/call, %.0f GB/s" % (un_s * 1e6, un_gbs))
+    if args.only_attn:
+        return
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nseq = 2
+        order = np.argsort(lens)
+        sample = sorted({int(order[len(order) // 2]), int(order[len(order) // 2 + 1])})[:nseq]
+        rows = [(b, t, h) for b in sample for t in range(S) for h in range(lp.Hq)]
+        threads = oracle.num_threads()
+        c0 = time.perf_counter()
+        for i in range(NL):
+            oracle.block_attn(lp.pools[i], rows=rows, q=lp.q[0][i], k_blk=lp.k_blk[0][i],
+                              v_blk=lp.v_blk[0][i])
+        c_attn = time.perf_counter() - c0
+        c1 = time.perf_counter()
+        sub = np.concatenate([lp.logits[0][b * S:(b + 1) * S] for b in sample])
+        oracle.unmask(sub, np.ones((len(sample), S), np.uint8), None, 4)
+        c_un = time.perf_counter() - c1
+        tok_sample = int((lens[sample] + S).sum())
+        tok_all = int((lens + S).sum())
+        step_s = c_attn * tok_all / tok_sample + c_un * B / len(sample)
+        cpu = {"value": 1.0 / step_s, "unit": "denoise-steps/s", "cores": threads, "kind": "oracle",
+               "sample": ("fp64 C oracle (OpenMP, %d threads): step-0 attention of %d sequences "
+                          "(L=%s) over all 6 layers (%d query rows) plus their unmask rows, %.1f s; "
+                          "scaled to the whole batch by context tokens (attention) and rows (unmask)"
+                          % (threads, len(sample), [int(lens[b]) for b in sample], len(rows) * NL,
+                             c_attn + c_un))}
+        log("cpu oracle: %.2f s per denoise step (extrapolated)" % step_s)
+
+    steps_per_s = T / block_s
+    traffic = read_traffic(attn_bytes)
+    res = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "denoise-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": block_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("denoise loop for one 16-token block: B=32, 6 attention layers, "
+                                "H_q=32, H_kv=2, D=128, paged bf16 KV (256-token pages), ctx "
+                                "U{2048..8192 step 16}, T=4 steps, unmask on fp32 [512, 131072]"),
+                   "global_batch": B, "block": S, "layers": NL, "denoise_steps_per_step": T,
+                   "vocab": V, "mean_ctx_len": float(lens.mean()), "graph": graph is not None,
+                   "parallelism": "none (1 GPU)", "seed": lp.seed},
+        "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "tt_block_attn (split + combine launches)",
+                     "us_per_launch": attn_s * 1e6, "alg_bytes_per_launch": attn_bytes,
+                     "tflops": attn_tfs, "mfma_frac": attn_tfs / MFMA_BF16_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+        "unmask": {"us_per_call": un_s * 1e6, "GB/s": un_gbs, "frac_hbm": un_gbs / HBM_PEAK_GBS},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

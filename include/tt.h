@@ -1,0 +1,194 @@
+/*
+ * tt.h -- C ABI of libtt.so: the TwoTower denoiser block-attention step, the
+ * confidence unmask that follows it, and the block-commit cache append, on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (page title, section):
+ *   "Nemotron-Labs-TwoTower: Diffusion Language Modeling with Pretrained
+ *    Autoregressive Context" (paperfeed.app review), "The idea: freeze the
+ *    reader, train the writer" and "Training and sampling";
+ *   "NVIDIA's Dual-Tower Diffusion Language Model Explained" (kongchang.com),
+ *    "The 'Sky Bridges' Between Layers" and "Generating Text in Parallel Like
+ *    Solving a Sudoku".
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  All tensors are contiguous,
+ *     row-major, last index fastest.
+ *   - Calls validate their arguments on the host, enqueue kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and return without waiting.
+ *     Results are valid once the stream has reached that point.
+ *   - Return value: TT_OK (0) or a negative tt_status.  On error nothing has
+ *     been enqueued and tt_last_error() holds a message for this thread.
+ *   - Values the host cannot see (ctx_lens[], page ids) are bounds-clamped on
+ *     the device so that bad values never fault; results are then
+ *     unspecified.  tt_kv_append skips a sequence whose target slots are not
+ *     all backed by valid pages.
+ *   - Calls are stateless apart from a per-thread error string; concurrent
+ *     calls on different streams must not share a workspace.
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TT_ABI_VERSION 1
+
+typedef enum tt_status {
+  TT_OK = 0,
+  TT_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  TT_ERR_SHAPE = -2,       /* a size is out of range or sizes are inconsistent  */
+  TT_ERR_DTYPE = -3,       /* unknown element type                              */
+  TT_ERR_UNSUPPORTED = -4, /* valid request this build does not implement       */
+  TT_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required        */
+  TT_ERR_NO_DEVICE = -6,   /* no usable HIP device                              */
+  TT_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch                 */
+} tt_status;
+
+typedef enum tt_dtype {
+  TT_BF16 = 0, /* bfloat16: MFMA path, head_dim 64 or 128                       */
+  TT_F32 = 1   /* float32: small-problem path, head_dim 1..256                  */
+} tt_dtype;
+
+/*
+ * Shape of one block-attention layer.
+ *
+ *   batch              B >= 0 sequences (B = 0 is a no-op), B <= 4096
+ *   block              S, tokens per noisy block, 1..64 (the pages use 16)
+ *   heads_q, heads_kv  H_q, H_kv >= 1, H_q % H_kv == 0; query head h reads
+ *                      KV head h / (H_q / H_kv) (contiguous GQA groups)
+ *   head_dim           D
+ *   page_size          tokens per cache page, a power of two in 16..4096
+ *   max_pages_per_seq  row stride of page_table (>= 1)
+ *   num_pages          P, pages in the pool (page ids must be < P)
+ *   max_ctx_len        host-side upper bound on every ctx_lens[b], at most
+ *                      max_pages_per_seq * page_size; sizes the launch
+ *   scale              softmax scale; <= 0 selects 1/sqrt(D)
+ *   dtype              tt_dtype of q, k_blk, v_blk, k_pages, v_pages, out
+ */
+typedef struct tt_attn_desc {
+  int32_t batch;
+  int32_t block;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t max_ctx_len;
+  float scale;
+  int32_t dtype;
+} tt_attn_desc;
+
+/* Workspace bytes tt_block_attn needs for this shape on the current device
+ * (0 is possible).  Returns a tt_status; *bytes is set on TT_OK. */
+int tt_block_attn_workspace_bytes(const tt_attn_desc *desc, size_t *bytes);
+
+/*
+ * Denoiser block attention for one layer ("The idea: freeze the reader,
+ * train the writer", paperfeed review; "The 'Sky Bridges' Between Layers",
+ * kongchang explainer).  For every sequence b, query head h and block slot t:
+ *
+ *   O[b,t,h,:] = softmax_j( scale * q[b,t,h,:] . Kcat_j ) @ Vcat
+ *
+ * where Kcat/Vcat concatenate the context tower's cached keys/values of the
+ * L_b = ctx_lens[b] committed tokens (gathered through page_table) with the
+ * S keys/values of the block itself.  No mask: the block is bidirectional
+ * inside, and causality across blocks comes from what the cache holds.
+ *
+ *   q          [B, S, H_q, D]
+ *   k_blk      [B, S, H_kv, D]        the block's own keys
+ *   v_blk      [B, S, H_kv, D]        the block's own values
+ *   k_pages    [P, H_kv, page_size, D]   cached keys, token-major per page
+ *   v_pages    [P, H_kv, D, page_size]   cached values, feature-major per page
+ *   page_table int32 [B, max_pages_per_seq]; entry j of row b is the page of
+ *              logical tokens [j*page_size, (j+1)*page_size); only the first
+ *              ceil(L_b / page_size) entries of a row are read
+ *   ctx_lens   int32 [B], 0 <= L_b <= max_ctx_len
+ *   out        [B, S, H_q, D]; bf16 results are rounded to nearest even
+ *   workspace  device scratch of tt_block_attn_workspace_bytes() bytes
+ *              (may be NULL if that is 0); no initial contents required
+ *
+ * bf16 path: Q.K^T and P.V on bf16 MFMA with fp32 accumulation, fp32 online
+ * softmax, probabilities rounded to bf16 for P.V.  f32 path: fp32 throughout.
+ * k_pages, v_pages and page_table may be NULL only when max_ctx_len == 0.
+ */
+int tt_block_attn(const tt_attn_desc *desc, const void *q, const void *k_blk,
+                  const void *v_blk, const void *k_pages, const void *v_pages,
+                  const int32_t *page_table, const int32_t *ctx_lens, void *out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Block commit: the context cache ingests a resolved block ("The idea: freeze
+ * the reader, train the writer", paperfeed review: once a block is resolved
+ * it is committed and the context tower's caches are updated).  For every
+ * sequence b with L_b = ctx_lens[b], writes k_blk[b,t]/v_blk[b,t] (t < S) to
+ * logical positions L_b + t of the paged pool (keys token-major, values
+ * feature-major, bit-exact copies) and sets ctx_lens[b] = L_b + S.
+ *
+ * The caller provides the pages: page_table must map every position up to
+ * L_b + S - 1.  A sequence whose target positions exceed
+ * max_pages_per_seq * page_size or map to an invalid page id is left
+ * untouched (no write, ctx_lens[b] unchanged).  desc->max_ctx_len is not used
+ * here; the caller raises it by S for later tt_block_attn calls.
+ */
+int tt_kv_append(const tt_attn_desc *desc, const void *k_blk, const void *v_blk,
+                 void *k_pages, void *v_pages, const int32_t *page_table,
+                 int32_t *ctx_lens, void *stream);
+
+/* tt_unmask flags */
+#define TT_UNMASK_UPDATE_MASK 1u /* clear mask[b,t] where commit_out[b,t] = 1 */
+
+/* Workspace bytes tt_unmask needs (0 is possible).  Returns a tt_status. */
+int tt_unmask_workspace_bytes(int32_t batch, int32_t block, int32_t vocab, size_t *bytes);
+
+/*
+ * Confidence unmask ("Training and sampling", paperfeed review; "Generating
+ * Text in Parallel Like Solving a Sudoku", kongchang explainer): predict
+ * every masked slot in parallel and commit the confident ones; committed
+ * slots stay fixed.  Count form of the commit rule.  For every row
+ * r = b*S + t of logits:
+ *
+ *   ids_out[r]  = smallest v with logits[r,v] == max_v logits[r,v]
+ *   conf[r]     = 1 / sum_v exp(logits[r,v] - max)   (max-softmax probability)
+ *
+ * and per sequence b the k_eff = clamp(k_b, 0, #masked_b) masked slots with
+ * the highest conf are committed (equal conf: lower slot first), where
+ * k_b = k_commit[b], or ceil(#masked_b / remaining_steps) when k_commit is
+ * NULL.  commit_out[r] = 1 exactly on those slots.
+ *
+ *   logits     float32 [B*S, V]; finite values or -inf, at least one finite
+ *              value per row
+ *   mask       uint8 [B, S], nonzero = masked; read-only unless flags has
+ *              TT_UNMASK_UPDATE_MASK (then cleared where committed)
+ *   k_commit   int32 [B] or NULL
+ *   remaining_steps  >= 1 when k_commit is NULL, else ignored
+ *   batch, block, vocab  B >= 0, 1 <= S <= 64, V >= 1
+ *   ids_out    int32 [B, S]
+ *   commit_out uint8 [B, S]
+ *   conf_out   float32 [B, S] or NULL
+ */
+int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit,
+              int32_t remaining_steps, int32_t batch, int32_t block, int32_t vocab,
+              int32_t *ids_out, uint8_t *commit_out, float *conf_out, uint32_t flags,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *tt_status_str(int status);
+
+/* Detailed message of the last failed call on this thread ("" if none). */
+const char *tt_last_error(void);
+
+/* TT_ABI_VERSION of the loaded library. */
+int tt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_H */

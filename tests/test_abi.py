@@ -1,0 +1,163 @@
+"""Host-side checks of libtt.so that need no GPU: it loads, exports every
+function include/tt.h declares, and its argument validation returns the
+documented status before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import two_tower_attention_amd as tt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tt.h")
+
+FAKE = ctypes.c_void_p(1 << 20)     # aligned, never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tt.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return tt.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(tt.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.tt_abi_version() == 1
+    for code in range(0, -8, -1):
+        s = tt.tt_status_str(code)
+        assert s.startswith("TT_"), s
+    assert "unknown" in tt.tt_status_str(-99)
+
+
+def good_desc(**kw):
+    d = dict(B=2, S=16, Hq=32, Hkv=2, D=128, page_size=256, max_pages=4, num_pages=8,
+             max_ctx_len=1000, scale=0.0, dtype="bf16")
+    d.update(kw)
+    return tt.make_desc(**d)
+
+
+BAD = [
+    ("dtype", dict(dtype="bf16"), {"dtype": 7}, -3),
+    ("batch", {}, {"batch": -1}, -2),
+    ("batch_big", {}, {"batch": 5000}, -2),
+    ("block0", {}, {"block": 0}, -2),
+    ("block65", {}, {"block": 65}, -2),
+    ("gqa", {}, {"heads_q": 30, "heads_kv": 4}, -2),
+    ("page_not_pow2", {}, {"page_size": 48}, -2),
+    ("page_small", {}, {"page_size": 8}, -2),
+    ("no_pages", {}, {"num_pages": 0}, -2),
+    ("ctx_over_capacity", {}, {"max_ctx_len": 4 * 256 + 1}, -2),
+    ("head_dim_bf16", {}, {"head_dim": 96}, -4),
+    ("head_dim_f32", dict(dtype="f32"), {"head_dim": 300}, -4),
+]
+
+
+@pytest.mark.parametrize("name,base,patch,code", BAD, ids=[b[0] for b in BAD])
+def test_desc_validation(lib, name, base, patch, code):
+    d = good_desc(**base)
+    for k, v in patch.items():
+        setattr(d, k, v)
+    n = ctypes.c_size_t(0)
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == code
+    assert tt.tt_last_error() != ""
+    st = lib.tt_block_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, ctypes.c_size_t(1 << 30), None)
+    assert st == code
+    st = lib.tt_kv_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == code
+
+
+def test_null_pointers(lib):
+    d = good_desc()
+    args = [FAKE] * 8
+    for i in (0, 1, 2, 6, 7):       # q, k_blk, v_blk, ctx_lens, out
+        a = list(args)
+        a[i] = None
+        assert lib.tt_block_attn(ctypes.byref(d), *a, FAKE, ctypes.c_size_t(1 << 30), None) == -1
+    a = list(args)
+    a[3] = None                     # k_pages with a context
+    assert lib.tt_block_attn(ctypes.byref(d), *a, FAKE, ctypes.c_size_t(1 << 30), None) == -1
+    d0 = good_desc(max_ctx_len=0)   # without context the pool may be NULL
+    a[4] = a[5] = None
+    st = lib.tt_block_attn(ctypes.byref(d0), *a, FAKE, ctypes.c_size_t(1 << 30), None)
+    assert st in (0, -6)            # OK on a GPU machine, no device here
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d), None) == -1
+
+
+def test_misaligned_pointer(lib):
+    d = good_desc()
+    bad = ctypes.c_void_p((1 << 20) + 2)
+    st = lib.tt_block_attn(ctypes.byref(d), bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           ctypes.c_size_t(1 << 30), None)
+    assert st == -4
+
+
+def test_batch_zero_is_noop(lib):
+    d = good_desc(B=0)
+    assert lib.tt_block_attn(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                             None, 0, None) == 0
+    n = ctypes.c_size_t(7)
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0 and n.value == 0
+
+
+def test_workspace_sizes(lib):
+    n = ctypes.c_size_t(0)
+    d = good_desc()
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value > 0 and n.value % 16 == 0
+    d32 = good_desc(dtype="f32", D=64)
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d32), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.tt_unmask_workspace_bytes(32, 16, 131072, ctypes.byref(n)) == 0
+    assert n.value >= 32 * 16 * 16
+
+
+def test_workspace_too_small(lib):
+    d = good_desc()
+    st = lib.tt_block_attn(ctypes.byref(d), *([FAKE] * 8), FAKE, ctypes.c_size_t(16), None)
+    assert st in (-5, -6)           # size is checked after the device query
+
+
+UNMASK_BAD = [
+    ("block0", dict(S=0), -2),
+    ("block65", dict(S=65), -2),
+    ("vocab0", dict(V=0), -2),
+    ("rows", dict(B=5000, S=16), -2),
+    ("remaining0", dict(rem=0, k=None), -2),
+    ("flags", dict(flags=2), -4),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", UNMASK_BAD, ids=[u[0] for u in UNMASK_BAD])
+def test_unmask_validation(lib, name, kw, code):
+    a = dict(B=2, S=16, V=1024, rem=1, k=FAKE, flags=0)
+    a.update(kw)
+    st = lib.tt_unmask(FAKE, FAKE, a["k"], a["rem"], a["B"], a["S"], a["V"], FAKE, FAKE, None,
+                       a["flags"], FAKE, ctypes.c_size_t(1 << 30), None)
+    assert st == code
+
+
+def test_unmask_nulls(lib):
+    st = lib.tt_unmask(None, FAKE, FAKE, 1, 2, 16, 1024, FAKE, FAKE, None, 0, FAKE,
+                       ctypes.c_size_t(1 << 30), None)
+    assert st == -1
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(tt.LibraryMissing):
+        tt.load_library(str(tmp_path / "nope.so"))

@@ -1,0 +1,62 @@
+// Internal declarations shared by the HIP sources of libtt.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tt.h"
+
+namespace tt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Largest batch the attention planner keeps in LDS (per-sequence prefix sums).
+constexpr int kMaxBatch = 4096;
+
+// Shape and launch plan of one bf16 block-attention call.
+struct AttnPlan {
+  int B, S, Hq, Hkv, g, D;
+  int page_size, max_pages, num_pages, max_ctx;
+  int qchunks;       // ceil(S*g / 256) query-row chunks per (b, h_kv)
+  int G;             // work-groups in the split launch
+  float scale_log2;  // softmax scale * log2(e)
+  size_t ws_bytes;   // workspace bytes
+};
+
+// Plans a bf16 call for a device with `cus` compute units.
+AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus);
+
+hipError_t launch_attn_bf16(const AttnPlan &p, const void *q, const void *k_blk,
+                            const void *v_blk, const void *k_pages, const void *v_pages,
+                            const int32_t *page_table, const int32_t *ctx_lens, void *out,
+                            void *workspace, hipStream_t stream);
+
+hipError_t launch_attn_f32(const tt_attn_desc &d, float scale, const float *q,
+                           const float *k_blk, const float *v_blk, const float *k_pages,
+                           const float *v_pages, const int32_t *page_table,
+                           const int32_t *ctx_lens, float *out, hipStream_t stream);
+
+hipError_t launch_kv_append(const tt_attn_desc &d, const void *k_blk, const void *v_blk,
+                            void *k_pages, void *v_pages, const int32_t *page_table,
+                            int32_t *ctx_lens, hipStream_t stream);
+
+struct UnmaskPlan {
+  int B, S, V;
+  int chunks;       // vocabulary chunks per row
+  int chunk_len;    // elements per chunk (multiple of 4)
+  size_t ws_bytes;
+};
+
+UnmaskPlan plan_unmask(int B, int S, int V);
+
+hipError_t launch_unmask(const UnmaskPlan &p, const float *logits, uint8_t *mask,
+                         const int32_t *k_commit, int remaining_steps, int32_t *ids,
+                         uint8_t *commit, float *conf, uint32_t flags, void *workspace,
+                         hipStream_t stream);
+
+}  // namespace tt

@@ -1,0 +1,193 @@
+// Confidence unmask ("Training and sampling", paperfeed review; "Generating
+// Text in Parallel Like Solving a Sudoku", kongchang explainer): for every
+// row of logits the greedy id (lowest index among equal maxima) and its
+// softmax probability 1/Z, Z = sum_v exp(l_v - max); then per sequence the
+// k most confident masked slots are committed (equal confidence: lower slot).
+//
+// Kernel 1 (rowreduce) streams the fp32 logits once, HBM-bound: each work-
+// group reduces one vocabulary chunk of one row to (max, lowest argmax,
+// sum exp(l - max)) with an online rescale, 16-byte loads, wave shuffles and
+// LDS.  Kernel 2 (commit) gives one wave to a sequence: lane t merges the
+// chunk partials of slot t, then ranks the masked slots by (conf desc, slot
+// asc) and commits those ranked below k.
+#include <limits.h>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Part {
+  float m;   // max
+  float s;   // sum exp(l - m)
+  int idx;   // lowest index attaining m
+  int pad;
+};
+
+// exp(x - m) for x <= m; m == -inf only when every x seen is -inf (-> 0).
+__device__ __forceinline__ float ex(float x, float m) {
+  return __builtin_amdgcn_exp2f((x - m) * kLog2e);
+}
+
+struct Acc {
+  float m, s;
+  int idx;
+  __device__ void init() { m = -INFINITY; s = 0.f; idx = INT_MAX; }
+  // Four consecutive elements starting at index i (in increasing order).
+  __device__ __forceinline__ void add4(float x0, float x1, float x2, float x3, int i) {
+    const float mx = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+    if (mx > m) {
+      idx = i + (x0 == mx ? 0 : x1 == mx ? 1 : x2 == mx ? 2 : 3);
+      s = (m == -INFINITY) ? 0.f : s * ex(m, mx);
+      m = mx;
+    }
+    const float mm = m == -INFINITY ? 0.f : m;
+    s += ex(x0, mm) + ex(x1, mm) + ex(x2, mm) + ex(x3, mm);
+  }
+  __device__ __forceinline__ void add1(float x, int i) {
+    if (x > m) {
+      idx = i;
+      s = (m == -INFINITY) ? 0.f : s * ex(m, x);
+      m = x;
+    }
+    s += ex(x, m == -INFINITY ? 0.f : m);
+  }
+  // Merge another partial; on equal maxima keep the lower index.
+  __device__ __forceinline__ void merge(float m2, float s2, int i2) {
+    const float M = fmaxf(m, m2);
+    const float a = (s == 0.f) ? 0.f : s * ex(m, M);
+    const float b = (s2 == 0.f) ? 0.f : s2 * ex(m2, M);
+    idx = (m2 > m) ? i2 : (m > m2) ? idx : min(idx, i2);
+    m = M;
+    s = a + b;
+  }
+};
+
+__global__ __launch_bounds__(kThreads) void unmask_rowreduce_kernel(const float *logits, int V,
+                                                                    int chunk_len, int chunks,
+                                                                    int vec, Part *parts) {
+  const int c = blockIdx.x, r = blockIdx.y;
+  const float *row = logits + (size_t)r * V;
+  const int begin = c * chunk_len;
+  const int end = min(begin + chunk_len, V);
+  const int tid = threadIdx.x;
+  Acc a;
+  a.init();
+  if (vec) {  // V % 4 == 0 and 16-byte aligned rows; chunk_len % 4 == 0
+    const int stride = 4 * kThreads;
+    int i = begin + 4 * tid;
+    for (; i + (kUnroll - 1) * stride < end; i += kUnroll * stride) {
+      float4 x[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) x[u] = *(const float4 *)(row + i + u * stride);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) a.add4(x[u].x, x[u].y, x[u].z, x[u].w, i + u * stride);
+    }
+    for (; i < end; i += stride) {
+      const float4 x = *(const float4 *)(row + i);
+      a.add4(x.x, x.y, x.z, x.w, i);
+    }
+  } else {
+    for (int i = begin + tid; i < end; i += kThreads) a.add1(row[i], i);
+  }
+  // wave reduction
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(a.m, o, 64);
+    const float s2 = __shfl_xor(a.s, o, 64);
+    const int i2 = __shfl_xor(a.idx, o, 64);
+    a.merge(m2, s2, i2);
+  }
+  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
+  __shared__ int si[kThreads / 64];
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) { sm[wave] = a.m; ss[wave] = a.s; si[wave] = a.idx; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / 64; ++w) a.merge(sm[w], ss[w], si[w]);
+    Part pt;
+    pt.m = a.m; pt.s = a.s; pt.idx = a.idx; pt.pad = 0;
+    parts[(size_t)r * chunks + c] = pt;
+  }
+}
+
+__global__ __launch_bounds__(64) void unmask_commit_kernel(const Part *parts, int chunks, int S,
+                                                           uint8_t *mask, const int32_t *k_commit,
+                                                           int remaining, int32_t *ids,
+                                                           uint8_t *commit, float *conf,
+                                                           uint32_t flags) {
+  __shared__ float cs[64];
+  __shared__ int ms[64];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const size_t r = (size_t)b * S + t;
+  float c = 0.f;
+  int id = 0, mk = 0;
+  if (t < S) {
+    Acc a;
+    a.init();
+    for (int k = 0; k < chunks; ++k) {
+      const Part pt = parts[r * chunks + k];
+      a.merge(pt.m, pt.s, pt.idx);
+    }
+    c = 1.f / a.s;
+    id = a.idx == INT_MAX ? 0 : a.idx;
+    mk = mask[r] != 0;
+  }
+  cs[t] = c;
+  ms[t] = mk;
+  __syncthreads();
+  int n = 0;
+  for (int u = 0; u < S; ++u) n += ms[u];
+  int kb = k_commit ? k_commit[b] : (n + remaining - 1) / remaining;
+  kb = min(max(kb, 0), n);
+  if (t < S) {
+    int rank = 0;
+    for (int u = 0; u < S; ++u)
+      rank += (ms[u] && (cs[u] > c || (cs[u] == c && u < t))) ? 1 : 0;
+    const int com = (mk && rank < kb) ? 1 : 0;
+    ids[r] = id;
+    commit[r] = (uint8_t)com;
+    if (conf) conf[r] = c;
+    if ((flags & TT_UNMASK_UPDATE_MASK) && com) mask[r] = 0;
+  }
+}
+
+}  // namespace
+
+UnmaskPlan plan_unmask(int B, int S, int V) {
+  UnmaskPlan p{};
+  p.B = B; p.S = S; p.V = V;
+  const long rows = (long)B * S;
+  const int per_wg = 4 * kThreads * kUnroll;  // elements one pass of a work-group covers
+  const int max_chunks = (V + per_wg - 1) / per_wg;
+  long want = rows > 0 ? (2048 + rows - 1) / rows : 1;  // aim for >= 2048 work-groups
+  if (want > max_chunks) want = max_chunks;
+  if (want < 1) want = 1;
+  int chunk_len = (int)((V + want - 1) / want);
+  chunk_len = (chunk_len + 3) & ~3;
+  p.chunk_len = chunk_len;
+  p.chunks = (V + chunk_len - 1) / chunk_len;
+  p.ws_bytes = (size_t)rows * p.chunks * sizeof(Part);
+  return p;
+}
+
+hipError_t launch_unmask(const UnmaskPlan &p, const float *logits, uint8_t *mask,
+                         const int32_t *k_commit, int remaining_steps, int32_t *ids,
+                         uint8_t *commit, float *conf, uint32_t flags, void *workspace,
+                         hipStream_t stream) {
+  Part *parts = (Part *)workspace;
+  const int vec = (p.V % 4 == 0) && (((uintptr_t)logits & 15) == 0);
+  hipLaunchKernelGGL(unmask_rowreduce_kernel, dim3(p.chunks, p.B * p.S), dim3(kThreads), 0,
+                     stream, logits, p.V, p.chunk_len, p.chunks, vec, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(unmask_commit_kernel, dim3(p.B), dim3(64), 0, stream, parts, p.chunks, p.S,
+                     mask, k_commit, remaining_steps, ids, commit, conf, flags);
+  return hipGetLastError();
+}
+
+}  // namespace tt
