@@ -19,12 +19,14 @@
 // partials.  The plan is rebuilt on the device from ctx_lens, so the host
 // never needs the lengths.
 //
-// Per work-group: 256 query rows, 32 * kQB of them per wave.
-// Per tile: K (token-major) and V^T (feature-major, as stored in the pool) are
-// staged through LDS; S^T = K . Q^T and O^T += V^T . P^T run on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, Q stays in registers, and
-// the online softmax works in the log2 domain with a lazily updated
-// reference maximum (the accumulators are only rescaled when the running max
+// Per work-group: 8 waves, 32 query rows each.  Context tiles stream from HBM
+// straight into a ring of kStages LDS buffers with global_load_lds_dwordx4
+// (no register staging); page ids of the range are cached in LDS first, so
+// the tile loop issues no other vector-memory operation and the ring is
+// synchronised with exact vmcnt waits.  Per tile: S^T = K . Q^T and
+// O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 (fp32 accumulate), Q held in
+// registers, online softmax in the log2 domain with a lazily updated
+// reference maximum (accumulators are rescaled only when the running max
 // grows by more than 2^8).
 #include <float.h>
 
@@ -35,24 +37,32 @@ namespace {
 
 constexpr int kTile = 64;        // keys per tile
 constexpr int kQRows = 256;      // query rows per unit
-constexpr int kQB = 1;           // 32-row query blocks per wave
+#ifndef TT_ATTN_QB
+#define TT_ATTN_QB 1
+#endif
+#ifndef TT_ATTN_STAGES
+#define TT_ATTN_STAGES 4
+#endif
+constexpr int kQB = TT_ATTN_QB;  // 32-row query blocks per wave
 constexpr int kThreads = 64 * (kQRows / 32) / kQB;  // waves x 64 lanes
 constexpr int kCombineThreads = kQRows;
+constexpr int kStages = TT_ATTN_STAGES;  // LDS ring depth (tiles in flight + 1)
+constexpr int kPageCache = 1024; // page ids cached per sub-range
 constexpr int kMinTiles = 8;     // smallest range worth a work-group
 constexpr float kLazy = 8.0f;    // rescale when max grows by > 2^kLazy
 
 template <int D>
 struct Geo {
-  static constexpr int KS = D / 16;                     // MFMA k-steps over D
-  static constexpr int DB = D / 32;                     // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;                    // LDS row pitch of K (elements)
-  static constexpr int VROW = kTile + 8;                // LDS row pitch of V^T
-  static constexpr int KCH = D / 8;                     // 16-byte chunks per key row
-  static constexpr int KPT = kTile * KCH / kThreads;    // key chunks per thread
+  static constexpr int KS = D / 16;                       // MFMA k-steps over D
+  static constexpr int DB = D / 32;                       // 32-row blocks of O^T
+  static constexpr int KCH = D / 8;                       // 16-byte chunks per key row
+  static constexpr int KPT = kTile * KCH / kThreads;      // key chunks per thread
   static constexpr int VPT = D * (kTile / 8) / kThreads;  // value chunks per thread
-  static constexpr int K_ELEMS = kTile * KROW;
-  static constexpr int V_ELEMS = D * VROW;
-  static constexpr size_t LDS_TILE_BYTES = (size_t)(K_ELEMS + V_ELEMS) * 2;
+  static constexpr int LPT = KPT + VPT;                   // direct loads per thread per tile
+  static constexpr int K_BYTES = kTile * D * 2;           // key tile [64][D]
+  static constexpr int V_BYTES = D * kTile * 2;           // value tile [D][64]
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static constexpr size_t RING_BYTES = (size_t)kStages * STAGE_BYTES;
   static_assert(KPT >= 1 && VPT >= 1, "tile too small for the work-group");
 };
 
@@ -135,6 +145,19 @@ __device__ __forceinline__ int pi_row(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// LDS swizzles (16-byte slots).  Key tile: row r (D*2 bytes) keeps chunk c in
+// slot c ^ (r mod KCH).  Value tile: row d (128 bytes) keeps token-chunk c in
+// slot c ^ fv(d).  Each keeps the MFMA operand reads (32 consecutive rows,
+// one chunk) free of bank conflicts.
+template <int D>
+__device__ __forceinline__ int k_off(int r, int c) {
+  return r * (D * 2) + 16 * (c ^ (r & (Geo<D>::KCH - 1)));
+}
+__device__ __forceinline__ int v_off(int d, int c) {
+  const int f = (d & 7) ^ ((d >> 3) & 1);
+  return d * (kTile * 2) + 16 * (c ^ f);
+}
+
 __device__ __forceinline__ int clamp_page(int pg, int num_pages) {
   return min(max(pg, 0), num_pages - 1);
 }
@@ -151,68 +174,110 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int n) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__device__ __forceinline__ uint4 sel(bool c, uint4 a) {
-  return c ? a : make_uint4(0, 0, 0, 0);
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Work-group barrier that orders LDS only.  __syncthreads() also fences
+// global memory, which makes the compiler drain every outstanding vector
+// load (vmcnt(0)) -- including the direct-to-LDS loads of tiles still in
+// flight.  Tile arrival is awaited explicitly with wait_tiles() instead.
+// The empty asm statements only stop the compiler from moving memory
+// accesses across the barrier; lgkmcnt(0) completes this wave's LDS
+// reads/writes before it signals arrival.
+constexpr int lgkm0_imm() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(lgkm0_imm());
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-template <int D>
-struct TileRegs {
-  uint4 k[Geo<D>::KPT];
-  uint4 v[Geo<D>::VPT];
-};
+// vmcnt-only s_waitcnt immediate (gfx9 encoding; expcnt/lgkmcnt left at max).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-// Global -> registers for context tile i of unit u (u.L >= 1 whenever a
-// context tile exists).  Addresses past the context are clamped into it and the
-// loaded values replaced by zeros, so the loads are branch-free.  `tile_page`
-// is the physical page of the whole tile when page_size >= kTile (pages then
-// never straddle a tile), else -1 and each chunk looks its page up.
+// Wait until at most `tiles_after` tiles' worth of direct loads are in flight.
 template <int D>
-__device__ __forceinline__ void load_ctx_tile(const Params &p, const Unit &u, int i,
-                                              int tile_page, TileRegs<D> &r) {
+__device__ __forceinline__ void wait_tiles(int tiles_after) {
+  constexpr int L = Geo<D>::LPT;
+  if (tiles_after <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  else if (tiles_after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+  else if (tiles_after == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * L));
+  static_assert(3 * Geo<D>::LPT < 64, "vmcnt range");
+  static_assert(kStages <= 4, "wait_tiles covers up to 3 tiles in flight");
+}
+
+// Issue the direct HBM->LDS loads of context tile i into `stage`.  Each wave
+// instruction fills 1 KiB of LDS contiguously (lane l -> bytes 16l..16l+15),
+// so lane l fetches whichever key/value chunk the swizzled layout puts there.
+// Positions past the context are clamped to a valid token: keys there are
+// masked by score, values are zeroed in LDS before use.
+template <int D>
+__device__ __forceinline__ void issue_tile(const Params &p, const Unit &u, int i,
+                                           unsigned char *stage, const int *pcache, int pbase) {
   using G = Geo<D>;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tok0 = i * kTile;
   const int pmask = p.page_size - 1;
-  const int32_t *pt = p.page_table + (size_t)u.b * p.max_pages;
 #pragma unroll
   for (int kk = 0; kk < G::KPT; ++kk) {
-    const int idx = tid + kThreads * kk;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    const int pos = tok0 + row;
-    const bool valid = pos < u.L;
-    const int posc = valid ? pos : u.L - 1;
-    const int pg = tile_page >= 0 ? tile_page : clamp_page(pt[posc >> p.lps], p.num_pages);
-    const uint4 x = *(const uint4 *)(p.k_pages +
-                                     (((size_t)pg * p.Hkv + u.h) * p.page_size + (posc & pmask)) * D +
-                                     8 * c);
-    r.k[kk] = sel(valid, x);
+    const int slot = kk * kThreads + tid;
+    const int r = slot / G::KCH, s = slot % G::KCH;
+    const int t = (r & ~31) | pi_row(r & 31);
+    const int c = s ^ (r & (G::KCH - 1));
+    const int pos = min(tok0 + t, u.L - 1);
+    const int pg = pcache[(pos >> p.lps) - pbase];
+    const __bf16 *src =
+        p.k_pages + (((size_t)pg * p.Hkv + u.h) * p.page_size + (pos & pmask)) * D + 8 * c;
+    __builtin_amdgcn_global_load_lds((const void *)src,
+                                     (lds_void *)(stage + (kk * kThreads + wave * 64) * 16), 16, 0,
+                                     0);
   }
 #pragma unroll
   for (int vv = 0; vv < G::VPT; ++vv) {
-    const int idx = tid + kThreads * vv;
-    const int d = idx >> 3, c = idx & 7;
+    const int slot = vv * kThreads + tid;
+    const int d = slot >> 3, s = slot & 7;
+    const int c = s ^ ((d & 7) ^ ((d >> 3) & 1));
     const int pos0 = tok0 + 8 * c;
-    const int n = u.L - pos0;  // valid tokens in this 8-token chunk (may be <= 0 or >= 8)
-    const int posc = n > 0 ? pos0 : ((u.L - 1) & ~7);
-    const int pg = tile_page >= 0 ? tile_page : clamp_page(pt[posc >> p.lps], p.num_pages);
-    const uint4 x = *(const uint4 *)(p.v_pages +
-                                     (((size_t)pg * p.Hkv + u.h) * D + d) * p.page_size + (posc & pmask));
-    r.v[vv] = keep_first(x, n);
+    const int pos = pos0 < u.L ? pos0 : ((u.L - 1) & ~7);
+    const int pg = pcache[(pos >> p.lps) - pbase];
+    const __bf16 *src = p.v_pages + (((size_t)pg * p.Hkv + u.h) * D + d) * p.page_size + (pos & pmask);
+    __builtin_amdgcn_global_load_lds(
+        (const void *)src, (lds_void *)(stage + G::K_BYTES + (vv * kThreads + wave * 64) * 16), 16,
+        0, 0);
   }
 }
 
-// Global -> registers for the block's own S keys/values (the unit's last tile).
+// Zero the value columns of tokens >= nvalid in a landed tile.
 template <int D>
-__device__ __forceinline__ void load_blk_tile(const Params &p, const Unit &u, TileRegs<D> &r) {
+__device__ __forceinline__ void zero_value_tail(unsigned char *stage, int nvalid) {
+  unsigned char *vs = stage + Geo<D>::K_BYTES;
+  for (int idx = threadIdx.x; idx < D * 8; idx += kThreads) {
+    const int d = idx >> 3, c = idx & 7;
+    const int n = nvalid - 8 * c;
+    if (n < 8) {
+      uint4 *ptr = (uint4 *)(vs + v_off(d, c));
+      *ptr = keep_first(*ptr, n);
+    }
+  }
+}
+
+// The block's own S keys/values into `stage` (registers -> LDS, values
+// transposed on the way); rows/columns >= S are zero.
+template <int D>
+__device__ __forceinline__ void stage_block_tile(const Params &p, const Unit &u,
+                                                 unsigned char *stage) {
   using G = Geo<D>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int kk = 0; kk < G::KPT; ++kk) {
     const int idx = tid + kThreads * kk;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    const int rc = min(row, p.S - 1);
-    const uint4 x = *(const uint4 *)(p.k_blk + (((size_t)u.b * p.S + rc) * p.Hkv + u.h) * D + 8 * c);
-    r.k[kk] = sel(row < p.S, x);
+    const int t = idx / G::KCH, c = idx % G::KCH;
+    const int tc = min(t, p.S - 1);
+    uint4 x = *(const uint4 *)(p.k_blk + (((size_t)u.b * p.S + tc) * p.Hkv + u.h) * D + 8 * c);
+    if (t >= p.S) x = make_uint4(0, 0, 0, 0);
+    const int r = (t & ~31) | pi_row(t & 31);
+    *(uint4 *)(stage + k_off<D>(r, c)) = x;
   }
   const uint16_t *vb = (const uint16_t *)p.v_blk;
 #pragma unroll
@@ -227,39 +292,7 @@ __device__ __forceinline__ void load_blk_tile(const Params &p, const Unit &u, Ti
       const uint32_t hi = vb[(((size_t)u.b * p.S + min(t1, p.S - 1)) * p.Hkv + u.h) * D + d];
       w[i2] = (t0 < p.S ? lo : 0u) | ((t1 < p.S ? hi : 0u) << 16);
     }
-    r.v[vv] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// Physical page of context tile i when one page covers the tile, else -1.
-__device__ __forceinline__ int tile_page_of(const Params &p, const Unit &u, int i) {
-  if (p.page_size < kTile || i >= u.T - 1) return -1;
-  return clamp_page(p.page_table[(size_t)u.b * p.max_pages + ((i * kTile) >> p.lps)], p.num_pages);
-}
-
-template <int D>
-__device__ __forceinline__ void load_tile(const Params &p, const Unit &u, int i, int tile_page,
-                                          TileRegs<D> &r) {
-  if (i < u.T - 1) load_ctx_tile<D>(p, u, i, tile_page, r);
-  else load_blk_tile<D>(p, u, r);
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &r, __bf16 *Ks, __bf16 *Vs) {
-  using G = Geo<D>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int kk = 0; kk < G::KPT; ++kk) {
-    const int idx = tid + kThreads * kk;
-    const int row = idx / G::KCH, c = idx % G::KCH;
-    const int lrow = (row & ~31) | pi_row(row & 31);
-    *(uint4 *)(Ks + lrow * G::KROW + 8 * c) = r.k[kk];
-  }
-#pragma unroll
-  for (int vv = 0; vv < G::VPT; ++vv) {
-    const int idx = tid + kThreads * vv;
-    const int d = idx >> 3, c = idx & 7;
-    *(uint4 *)(Vs + d * G::VROW + 8 * c) = r.v[vv];
+    *(uint4 *)(stage + G::K_BYTES + v_off(d, c)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -278,13 +311,192 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D>
-__device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool complete,
-                         int slot, __bf16 *Ks, __bf16 *Vs) {
+struct Acc {
+  f32x16 o[Geo<D>::DB][kQB];
+  float mref[kQB], lsum[kQB];
+};
+
+template <int D>
+struct PTile {
+  bf16x8 v[2][kQB][2];  // probabilities of a 64-key tile as P.V B-operands
+};
+
+// Scores and online softmax of one 64-key tile from `stage`.  The key
+// operands of each 32-key half are read from LDS before its score MFMAs
+// (sched_barrier keeps the compiler from sinking the reads next to their
+// uses, which would expose the LDS latency once per MFMA).  Rescales the accumulators when the running
+// max grows by more than 2^kLazy, then returns P rounded to bf16.
+template <int D>
+__device__ __forceinline__ void scores_softmax(const Params &p, const unsigned char *stage,
+                                               int nvalid, const bf16x8 (&qr)[kQB][Geo<D>::KS],
+                                               Acc<D> &A, PTile<D> &P) {
   using G = Geo<D>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31, hl = lane >> 5;
+  const unsigned char *Ks = stage;
+
+  f32x16 s[2][kQB];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    bf16x8 ka[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks)
+      ka[ks] = *(const bf16x8 *)(Ks + k_off<D>(32 * tb + ln, 2 * ks + hl));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) s[tb][qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+        s[tb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[qb][ks], s[tb][qb], 0, 0, 0);
+  }
+  // key index of accumulator register r in lane half hl: 32*tb + 16*(r/8) + 8*hl + r%8
+  if (nvalid < kTile) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * tb + 16 * (r >> 3) + 8 * hl + (r & 7);
+        if (key >= nvalid) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) s[tb][qb][r] = -INFINITY;
+        }
+      }
+  }
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tb][qb][r]);
+    mx = pair_max(mx);
+    const float mxs = mx * p.sl2;
+    const bool need = mxs > A.mref[qb] + kLazy;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float f = need ? __builtin_amdgcn_exp2f(A.mref[qb] - mxs) : 1.f;
+      if (need) A.mref[qb] = mxs;
+      A.lsum[qb] *= f;
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db) A.o[db][qb] *= f;
+    }
+    const float nm = -A.mref[qb];
+    float acc = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x16 e;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][r], p.sl2, nm));
+        acc += e[r];
+      }
+      f32x8 lo = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
+      f32x8 hi = {e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]};
+      P.v[tb][qb][0] = __builtin_convertvector(lo, bf16x8);
+      P.v[tb][qb][1] = __builtin_convertvector(hi, bf16x8);
+    }
+    A.lsum[qb] += acc;
+  }
+}
+
+// O^T += V^T . P^T for one tile; each half's value operands are read before
+// its MFMAs.
+template <int D>
+__device__ __forceinline__ void pv_tile(const unsigned char *stage, const PTile<D> &P, Acc<D> &A) {
+  using G = Geo<D>;
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31, hl = lane >> 5;
+  const unsigned char *Vs = stage + G::K_BYTES;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    bf16x8 va[2][G::DB];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+        va[cc][db] = *(const bf16x8 *)(Vs + v_off(32 * db + ln, 4 * tb + 2 * cc + hl));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          A.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], P.v[tb][qb][cc], A.o[db][qb], 0, 0, 0);
+  }
+}
+
+// Context tiles [i0, ctx_end) of unit u through the LDS ring, in sub-ranges
+// whose pages fit the page-id cache.  LAG selects the wave-group role.
+template <int D, bool LAG>
+__device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, int i0, int ctx_end,
+                                              unsigned char *ring, int *pcache,
+                                              const bf16x8 (&qr)[kQB][Geo<D>::KS], Acc<D> &A,
+                                              PTile<D> &P) {
+  using G = Geo<D>;
+  constexpr int kAhead = kStages - 2;  // tiles prefetched beyond the current one
+  const int sub = max(1, (kPageCache * p.page_size) / kTile - 1);
+  for (int c0 = i0; c0 < ctx_end; c0 += sub) {
+    const int c1 = min(c0 + sub, ctx_end);
+    const int pbase = (c0 * kTile) >> p.lps;
+    const int plast = (min(c1 * kTile, u.L) - 1) >> p.lps;
+    const int32_t *pt = p.page_table + (size_t)u.b * p.max_pages;
+    for (int k = threadIdx.x; k <= plast - pbase; k += kThreads)
+      pcache[k] = clamp_page(pt[pbase + k], p.num_pages);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (c0 + j < c1) issue_tile<D>(p, u, c0 + j, ring + (j % kStages) * G::STAGE_BYTES, pcache, pbase);
+    const unsigned char *prev = nullptr;
+    for (int i = c0; i < c1; ++i) {
+      wait_tiles<D>(min(kAhead - 1, c1 - 1 - i));
+      lds_barrier();   // tile i visible to all waves; tile i-2's stage free
+      unsigned char *stage = ring + ((i - c0) % kStages) * G::STAGE_BYTES;
+      if (i + kAhead < c1)
+        issue_tile<D>(p, u, i + kAhead, ring + ((i - c0 + kAhead) % kStages) * G::STAGE_BYTES,
+                      pcache, pbase);
+      const int nvalid = min(kTile, u.L - i * kTile);
+      if (nvalid < kTile) {
+        zero_value_tail<D>(stage, nvalid);
+        lds_barrier();
+      }
+      if (!LAG) {
+        scores_softmax<D>(p, stage, nvalid, qr, A, P);
+        pv_tile<D>(stage, P, A);
+      } else {
+        if (prev) pv_tile<D>(prev, P, A);
+        scores_softmax<D>(p, stage, nvalid, qr, A, P);
+        prev = stage;
+      }
+    }
+    if (LAG && prev) pv_tile<D>(prev, P, A);
+    lds_barrier();   // ring and page cache free for reuse
+  }
+}
+
+// One unit's tiles [i0, i1) on this work-group.
+//
+// Context tiles stream through the LDS ring.  The waves are split into two
+// groups that share the SIMDs (wave w and w + waves/2 sit on the same SIMD):
+// the lead group runs scores -> softmax -> P.V on tile i, the lag group runs
+// P.V of tile i-1 first and then scores -> softmax of tile i.  Within one
+// barrier interval the two waves on a SIMD are then in different phases, so
+// one wave's softmax (VALU) overlaps the other's MFMAs.  The lag group keeps
+// its probabilities for one tile; a tile's stage therefore stays live for two
+// iterations and only kStages - 2 tiles are prefetched.
+template <int D>
+__device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool complete,
+                         int slot, unsigned char *ring, int *pcache) {
+  using G = Geo<D>;
+  constexpr int kWaves = kThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ln = lane & 31, hl = lane >> 5;
   const int M = p.S * p.g;
   constexpr int WROWS = 32 * kQB;  // query rows per wave
+  const bool lag = wave >= kWaves / 2;
 
   // Q (B operand of S^T = K . Q^T): lane holds row ln of each 32-row block,
   // features 16*ks + 8*hl .. +7.
@@ -302,119 +514,35 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
       for (int ks = 0; ks < G::KS; ++ks) qr[qb][ks] = bf16x8{};
     }
   }
-
-  f32x16 o[G::DB][kQB];
+  Acc<D> A;
 #pragma unroll
   for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) o[db][qb] = f32x16{};
-  float mref[kQB], lsum[kQB];
+    for (int qb = 0; qb < kQB; ++qb) A.o[db][qb] = f32x16{};
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) { mref[qb] = -INFINITY; lsum[qb] = 0.f; }
+  for (int qb = 0; qb < kQB; ++qb) { A.mref[qb] = -INFINITY; A.lsum[qb] = 0.f; }
+  PTile<D> P;
 
-  TileRegs<D> regs;
-  load_tile<D>(p, u, i0, tile_page_of(p, u, i0), regs);
-  store_tile<D>(regs, Ks, Vs);
-  int next_page = tile_page_of(p, u, i0 + 1);
-  __syncthreads();
-
-  for (int i = i0; i < i1; ++i) {
-    const bool more = i + 1 < i1;
-    if (more) {
-      load_tile<D>(p, u, i + 1, next_page, regs);
-      next_page = tile_page_of(p, u, i + 2);
-    }
-    const int nvalid = (i < u.T - 1) ? min(kTile, u.L - i * kTile) : p.S;
-
-    // ---- S^T[key][query] for two 32-key blocks
-    f32x16 s[2][kQB];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) s[tb][qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
-        const bf16x8 a = *(const bf16x8 *)(Ks + (32 * tb + ln) * G::KROW + 16 * ks + 8 * hl);
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          s[tb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[qb][ks], s[tb][qb], 0, 0, 0);
-      }
-    }
-    // key index of accumulator register r in lane half hl: 32*tb + 16*(r/8) + 8*hl + r%8
-    if (nvalid < kTile) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * tb + 16 * (r >> 3) + 8 * hl + (r & 7);
-          if (key >= nvalid) {
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) s[tb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // ---- online softmax (log2 domain), P rounded to bf16
-    bf16x8 pk[2][kQB][2];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tb][qb][r]);
-      mx = pair_max(mx);
-      const float mxs = mx * p.sl2;
-      const bool need = mxs > mref[qb] + kLazy;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float f = need ? __builtin_amdgcn_exp2f(mref[qb] - mxs) : 1.f;
-        if (need) mref[qb] = mxs;
-        lsum[qb] *= f;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) o[db][qb] *= f;
-      }
-      const float nm = -mref[qb];
-      float acc = 0.f;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f32x16 e;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][r], p.sl2, nm));
-          acc += e[r];
-        }
-        f32x8 lo = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
-        f32x8 hi = {e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]};
-        pk[tb][qb][0] = __builtin_convertvector(lo, bf16x8);
-        pk[tb][qb][1] = __builtin_convertvector(hi, bf16x8);
-      }
-      lsum[qb] += acc;
-    }
-
-    // ---- O^T[d][query] += V^T . P^T
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) {
-          const bf16x8 a =
-              *(const bf16x8 *)(Vs + (32 * db + ln) * G::VROW + 32 * tb + 16 * cc + 8 * hl);
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[tb][qb][cc], o[db][qb], 0, 0, 0);
-        }
-
-    __syncthreads();
-    if (more) store_tile<D>(regs, Ks, Vs);
-    __syncthreads();
+  // ---- context tiles [i0, ctx_end): one loop instance per role, so that the
+  // register allocation of each is independent (same barrier sequence)
+  const int ctx_end = min(i1, u.T - 1);
+  if (lag) context_tiles<D, true>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
+  else context_tiles<D, false>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
+  // ---- the block's own S keys/values (the unit's last tile)
+  if (i1 == u.T) {
+    unsigned char *stage = ring;
+    stage_block_tile<D>(p, u, stage);
+    lds_barrier();
+    scores_softmax<D>(p, stage, p.S, qr, A, P);
+    pv_tile<D>(stage, P, A);
+    lds_barrier();
   }
 
   // ---- epilogue.  O^T accumulator register r of lane (hl, ln) in block db
   // holds feature 32*db + 8*(r/4) + 4*hl + r%4 of query row ln.
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    const float ltot = pair_sum(lsum[qb]);
+    const float ltot = pair_sum(A.lsum[qb]);
     const int qloc = wave * WROWS + qb * 32 + ln;
     const int qi = u.qc * kQRows + qloc;
     if (complete) {
@@ -426,8 +554,8 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            f32x4 v = {o[db][qb][4 * r4 + 0] * inv, o[db][qb][4 * r4 + 1] * inv,
-                       o[db][qb][4 * r4 + 2] * inv, o[db][qb][4 * r4 + 3] * inv};
+            f32x4 v = {A.o[db][qb][4 * r4 + 0] * inv, A.o[db][qb][4 * r4 + 1] * inv,
+                       A.o[db][qb][4 * r4 + 2] * inv, A.o[db][qb][4 * r4 + 3] * inv};
             *(bf16x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = __builtin_convertvector(v, bf16x4);
           }
       }
@@ -438,11 +566,11 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int d = 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3);
-          wo[(size_t)d * kQRows + qloc] = o[db][qb][r];
+          wo[(size_t)d * kQRows + qloc] = A.o[db][qb][r];
         }
       if (hl == 0) {
         float *wm = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
-        wm[0] = mref[qb];
+        wm[0] = A.mref[qb];
         wm[1] = ltot;
       }
     }
@@ -453,9 +581,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int scan[kThreads];
-  __bf16 *Ks = (__bf16 *)smem;
-  __bf16 *Vs = Ks + Geo<D>::K_ELEMS;
-  int *pre = (int *)(smem + Geo<D>::LDS_TILE_BYTES);
+  unsigned char *ring = smem;
+  int *pcache = (int *)(smem + Geo<D>::RING_BYTES);
+  int *pre = pcache + kPageCache;
   build_prefix<kThreads>(p, pre, scan);
   const int total = pre[p.B];
   const int R = (total + p.G - 1) / p.G;
@@ -466,18 +594,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
     const Unit u = locate(p, pre, t);
     const int i0 = t - u.start;
     const int i1 = min(t_end, u.start + u.T) - u.start;
-    run_unit<D>(p, u, i0, i1, i0 == 0 && i1 == u.T, 2 * blockIdx.x + (first ? 0 : 1), Ks, Vs);
+    run_unit<D>(p, u, i0, i1, i0 == 0 && i1 == u.T, 2 * blockIdx.x + (first ? 0 : 1), ring, pcache);
     first = false;
     t = u.start + i1;
   }
 }
 
-// One work-group per unit; merges the partials of units cut by a range
-// boundary: O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
+// Merges the partials of units cut by a range boundary:
+//   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w.
+// One work-group per (unit, 32-feature slice); thread = query row.  The
+// contributing slots are found once per work-group, then every partial load
+// is independent (coalesced across rows).
+constexpr int kMaxContrib = 1024;
+
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int scan[kCombineThreads];
+  __shared__ int slots[kMaxContrib];
   int *pre = (int *)smem;
   build_prefix<kCombineThreads>(p, pre, scan);
   const int upb = p.Hkv * p.qchunks;
@@ -489,47 +623,66 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(Params p)
   const int total = pre[p.B];
   const int R = (total + p.G - 1) / p.G;
   const int w_lo = us / R, w_hi = (ue - 1) / R;
-  if (w_lo == w_hi) return;  // finished in place
+  if (w_lo == w_hi) return;  // finished in place by one work-group
+  const int n = w_hi - w_lo + 1;
+  for (int k = threadIdx.x; k < n; k += kCombineThreads) {
+    const int w = w_lo + k;
+    slots[k] = 2 * w + (locate(p, pre, w * R).id == uid ? 0 : 1);
+  }
+  __syncthreads();
   const int qloc = threadIdx.x;
   const int qi = qc * kQRows + qloc;
   if (qi >= p.S * p.g) return;
 
   float M = -INFINITY;
-  for (int w = w_lo; w <= w_hi; ++w) {
-    const int slot = 2 * w + (locate(p, pre, w * R).id == uid ? 0 : 1);
-    M = fmaxf(M, p.ws_ml[((size_t)slot * kQRows + qloc) * 2]);
-  }
+  for (int k = 0; k < n; ++k) M = fmaxf(M, p.ws_ml[((size_t)slots[k] * kQRows + qloc) * 2]);
   float lt = 0.f;
-  for (int w = w_lo; w <= w_hi; ++w) {
-    const int slot = 2 * w + (locate(p, pre, w * R).id == uid ? 0 : 1);
-    const float *m = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
+  for (int k = 0; k < n; ++k) {
+    const float *m = p.ws_ml + ((size_t)slots[k] * kQRows + qloc) * 2;
     lt += __builtin_amdgcn_exp2f(m[0] - M) * m[1];
   }
   const float inv = 1.f / lt;
-  const int t = qi / p.g, j = qi % p.g;
-  __bf16 *dst = p.out + (((size_t)b * p.S + t) * p.Hq + h * p.g + j) * D;
-  for (int dc = 0; dc < D / 8; ++dc) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int w = w_lo; w <= w_hi; ++w) {
-      const int slot = 2 * w + (locate(p, pre, w * R).id == uid ? 0 : 1);
-      const float wt = __builtin_amdgcn_exp2f(p.ws_ml[((size_t)slot * kQRows + qloc) * 2] - M) * inv;
-      const float *src = p.ws_o + ((size_t)slot * D + 8 * dc) * kQRows + qloc;
+  const int d0 = 32 * blockIdx.y;
+  float acc[32];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wt * src[(size_t)e * kQRows];
-    }
-    f32x8 v = {acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7]};
-    *(bf16x8 *)(dst + 8 * dc) = __builtin_convertvector(v, bf16x8);
+  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+  for (int k = 0; k < n; ++k) {
+    const float wt = __builtin_amdgcn_exp2f(p.ws_ml[((size_t)slots[k] * kQRows + qloc) * 2] - M) * inv;
+    const float *src = p.ws_o + ((size_t)slots[k] * D + d0) * kQRows + qloc;
+    float x[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) x[e] = src[(size_t)e * kQRows];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) acc[e] += wt * x[e];
+  }
+  const int t = qi / p.g, j = qi % p.g;
+  __bf16 *dst = p.out + (((size_t)b * p.S + t) * p.Hq + h * p.g + j) * D + d0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    f32x8 v = {acc[8 * c + 0], acc[8 * c + 1], acc[8 * c + 2], acc[8 * c + 3],
+               acc[8 * c + 4], acc[8 * c + 5], acc[8 * c + 6], acc[8 * c + 7]};
+    *(bf16x8 *)(dst + 8 * c) = __builtin_convertvector(v, bf16x8);
   }
 }
 
 template <int D>
 hipError_t launch_d(const Params &prm, hipStream_t stream) {
   const size_t pre_bytes = (size_t)(prm.B + 1) * sizeof(int);
-  hipLaunchKernelGGL(attn_split_kernel<D>, dim3(prm.G), dim3(kThreads),
-                     Geo<D>::LDS_TILE_BYTES + pre_bytes, stream, prm);
+  const size_t split_lds = Geo<D>::RING_BYTES + kPageCache * sizeof(int) + pre_bytes;
+  static bool attr_done = false;   // benign race: every caller sets the same value
+  if (!attr_done) {
+    const hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<D>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)(Geo<D>::RING_BYTES + kPageCache * sizeof(int) +
+                                                   (kMaxBatch + 1) * sizeof(int)));
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(attn_split_kernel<D>, dim3(prm.G), dim3(kThreads), split_lds, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(prm.B * prm.Hkv * prm.qchunks), dim3(kCombineThreads),
+  hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(prm.B * prm.Hkv * prm.qchunks, D / 32),
+                     dim3(kCombineThreads),
                      pre_bytes, stream, prm);
   return hipGetLastError();
 }
@@ -548,6 +701,7 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus) {
   const long tiles = (long)p.B * p.Hkv * p.qchunks * ((p.max_ctx + kTile - 1) / kTile + 1);
   long G = (tiles + kMinTiles - 1) / kMinTiles;
   if (G > cus) G = cus;
+  if (G > 1024) G = 1024;  // the combine keeps one slot id per contributor in LDS
   if (G < 1) G = 1;
   p.G = (int)G;
   p.ws_bytes = (size_t)2 * G * ((size_t)p.D * kQRows + 2 * kQRows) * sizeof(float);
