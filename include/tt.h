@@ -58,7 +58,7 @@ typedef enum tt_dtype {
 /*
  * Shape of one block-attention layer.
  *
- *   batch              B >= 0 sequences (B = 0 is a no-op), B <= 4096
+ *   batch              B >= 0 sequences (B = 0 is a no-op), B <= 2048
  *   block              S, tokens per noisy block, 1..64 (the pages use 16)
  *   heads_q, heads_kv  H_q, H_kv >= 1, H_q % H_kv == 0; query head h reads
  *                      KV head h / (H_q / H_kv) (contiguous GQA groups)

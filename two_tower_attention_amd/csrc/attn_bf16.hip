@@ -45,10 +45,14 @@ constexpr int kQRows = 256;      // query rows per unit
 #endif
 constexpr int kQB = TT_ATTN_QB;  // 32-row query blocks per wave
 constexpr int kThreads = 64 * (kQRows / 32) / kQB;  // waves x 64 lanes
-constexpr int kCombineThreads = kQRows;
 constexpr int kStages = TT_ATTN_STAGES;  // LDS ring depth (tiles in flight + 1)
 constexpr int kPageCache = 1024; // page ids cached per sub-range
 constexpr int kMinTiles = 8;     // smallest range worth a work-group
+// Each unit carries kUnitPad virtual tiles after its real ones: they stand
+// for the unit's fixed cost (Q load, page-id cache, pipeline fill, block
+// tile, epilogue) so that ranges which cut unit boundaries get fewer real
+// tiles.  A virtual tile holds no work.
+constexpr int kUnitPad = 2;
 constexpr float kLazy = 8.0f;    // rescale when max grows by > 2^kLazy
 
 template <int D>
@@ -70,56 +74,51 @@ struct Params {
   const __bf16 *q, *k_blk, *v_blk, *k_pages, *v_pages;
   const int32_t *page_table, *ctx_lens;
   __bf16 *out;
-  float *ws_o;   // [2G][D][256] unnormalised O^T partials
+  int *ws_pre;   // [B+1] flat-tile prefix, published for the combine
+  float *ws_o;   // [2G][D*256] unnormalised O^T partials
   float *ws_ml;  // [2G][256][2]  (reference max in log2 units, sum)
   int B, S, Hq, Hkv, g, page_size, lps, max_pages, num_pages, max_ctx, qchunks, G;
   float sl2;
 };
 
-__device__ __forceinline__ int seq_len(const Params &p, int b) {
-  const int L = p.ctx_lens[b];
-  return min(max(L, 0), p.max_ctx);
-}
+// real tiles of a unit: context tiles plus the block tile
+__device__ __forceinline__ int real_tiles(int L) { return (L + kTile - 1) / kTile + 1; }
+__device__ __forceinline__ int seq_tiles(int L) { return real_tiles(L) + kUnitPad; }
 
-__device__ __forceinline__ int seq_tiles(int L) { return (L + kTile - 1) / kTile + 1; }
-
-// pre[b] = first flat tile of sequence b (all its units), pre[B] = total.
-template <int NT>
-__device__ void build_prefix(const Params &p, int *pre, int *scan) {
-  const int tid = threadIdx.x;
-  const int per = (p.B + NT - 1) / NT;
-  const int upb = p.Hkv * p.qchunks;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < p.B) local += seq_tiles(seq_len(p, b)) * upb;
-  }
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  int run = scan[tid] - local;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < p.B) {
-      pre[b] = run;
-      run += seq_tiles(seq_len(p, b)) * upb;
+// pre[b] = first flat tile of sequence b (all its units), pre[B] = total;
+// lens[b] = clamped context length.  One wave scans 64 sequences per step.
+__device__ void build_prefix(const Params &p, int *pre, int *lens) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int upb = p.Hkv * p.qchunks;
+    int carry = 0;
+    for (int base = 0; base < p.B; base += 64) {
+      const int b = base + lane;
+      const int L = b < p.B ? min(max(p.ctx_lens[b], 0), p.max_ctx) : 0;
+      const int t = b < p.B ? seq_tiles(L) * upb : 0;
+      int x = t;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (b < p.B) {
+        pre[b] = carry + x - t;
+        lens[b] = L;
+      }
+      carry += __shfl(x, 63, 64);
     }
+    if (lane == 0) pre[p.B] = carry;
   }
-  if (tid == NT - 1) pre[p.B] = scan[tid];
   __syncthreads();
 }
 
 struct Unit {
-  int b, h, qc, L, T, start, id;
+  int b, h, qc, L, T, nreal, start, id;
 };
 
 // The unit that owns flat tile t.
-__device__ Unit locate(const Params &p, const int *pre, int t) {
+__device__ Unit locate(const Params &p, const int *pre, const int *lens, int t) {
   int lo = 0, hi = p.B;  // pre[lo] <= t < pre[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -127,8 +126,9 @@ __device__ Unit locate(const Params &p, const int *pre, int t) {
   }
   Unit u;
   u.b = lo;
-  u.L = seq_len(p, lo);
+  u.L = lens[lo];
   u.T = seq_tiles(u.L);
+  u.nreal = real_tiles(u.L);
   const int ui = (t - pre[lo]) / u.T;
   u.h = ui / p.qchunks;
   u.qc = ui % p.qchunks;
@@ -279,20 +279,22 @@ __device__ __forceinline__ void stage_block_tile(const Params &p, const Unit &u,
     const int r = (t & ~31) | pi_row(t & 31);
     *(uint4 *)(stage + k_off<D>(r, c)) = x;
   }
-  const uint16_t *vb = (const uint16_t *)p.v_blk;
+  // values: token row t, features 8c..8c+7 loaded as one 16-byte chunk and
+  // scattered into the feature-major tile (token t = column t).
 #pragma unroll
-  for (int vv = 0; vv < G::VPT; ++vv) {
-    const int idx = tid + kThreads * vv;
-    const int d = idx >> 3, c = idx & 7;
-    uint32_t w[4];
+  for (int kk = 0; kk < G::KPT; ++kk) {
+    const int idx = tid + kThreads * kk;
+    const int t = idx / G::KCH, c = idx % G::KCH;
+    const int tc = min(t, p.S - 1);
+    uint4 x = *(const uint4 *)(p.v_blk + (((size_t)u.b * p.S + tc) * p.Hkv + u.h) * D + 8 * c);
+    if (t >= p.S) x = make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      const int t0 = 8 * c + 2 * i2, t1 = t0 + 1;
-      const uint32_t lo = vb[(((size_t)u.b * p.S + min(t0, p.S - 1)) * p.Hkv + u.h) * D + d];
-      const uint32_t hi = vb[(((size_t)u.b * p.S + min(t1, p.S - 1)) * p.Hkv + u.h) * D + d];
-      w[i2] = (t0 < p.S ? lo : 0u) | ((t1 < p.S ? hi : 0u) << 16);
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * c + e;
+      const uint16_t val = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      *(uint16_t *)(stage + G::K_BYTES + v_off(d, t >> 3) + 2 * (t & 7)) = val;
     }
-    *(uint4 *)(stage + G::K_BYTES + v_off(d, c)) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -525,11 +527,11 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
 
   // ---- context tiles [i0, ctx_end): one loop instance per role, so that the
   // register allocation of each is independent (same barrier sequence)
-  const int ctx_end = min(i1, u.T - 1);
+  const int ctx_end = min(i1, u.nreal - 1);
   if (lag) context_tiles<D, true>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
   else context_tiles<D, false>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
-  // ---- the block's own S keys/values (the unit's last tile)
-  if (i1 == u.T) {
+  // ---- the block's own S keys/values (the unit's last real tile)
+  if (i0 < u.nreal && i1 >= u.nreal) {
     unsigned char *stage = ring;
     stage_block_tile<D>(p, u, stage);
     lds_barrier();
@@ -560,13 +562,17 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
           }
       }
     } else {
-      float *wo = p.ws_o + (size_t)slot * D * kQRows;
+      // partial O^T in accumulator layout: float4 (registers 4*r4 .. 4*r4+3)
+      // of lane l at ((((wave*kQB + qb)*DB + db)*4 + r4)*64 + l); features
+      // 32*db + 8*r4 + 4*(l/32) + 0..3 of query row wave*WROWS + qb*32 + l%32
+      f32x4 *wo = (f32x4 *)(p.ws_o + (size_t)slot * D * kQRows);
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int d = 32 * db + 8 * (r >> 2) + 4 * hl + (r & 3);
-          wo[(size_t)d * kQRows + qloc] = A.o[db][qb][r];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = {A.o[db][qb][4 * r4], A.o[db][qb][4 * r4 + 1], A.o[db][qb][4 * r4 + 2],
+                           A.o[db][qb][4 * r4 + 3]};
+          wo[(((wave * kQB + qb) * G::DB + db) * 4 + r4) * 64 + lane] = v;
         }
       if (hl == 0) {
         float *wm = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
@@ -580,21 +586,26 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int scan[kThreads];
   unsigned char *ring = smem;
   int *pcache = (int *)(smem + Geo<D>::RING_BYTES);
   int *pre = pcache + kPageCache;
-  build_prefix<kThreads>(p, pre, scan);
+  int *lens = pre + p.B + 1;
+  build_prefix(p, pre, lens);
+  if (blockIdx.x == 0)
+    for (int k = threadIdx.x; k <= p.B; k += kThreads) p.ws_pre[k] = pre[k];
   const int total = pre[p.B];
   const int R = (total + p.G - 1) / p.G;
   const int t_begin = blockIdx.x * R;
   const int t_end = min(t_begin + R, total);
   bool first = true;
   for (int t = t_begin; t < t_end;) {
-    const Unit u = locate(p, pre, t);
+    const Unit u = locate(p, pre, lens, t);
     const int i0 = t - u.start;
     const int i1 = min(t_end, u.start + u.T) - u.start;
-    run_unit<D>(p, u, i0, i1, i0 == 0 && i1 == u.T, 2 * blockIdx.x + (first ? 0 : 1), ring, pcache);
+    // slot 0 holds the partial of the range's first unit, slot 1 its last
+    if (i0 < u.nreal)
+      run_unit<D>(p, u, i0, i1, i0 == 0 && i1 >= u.nreal, 2 * blockIdx.x + (first ? 0 : 1), ring,
+                  pcache);
     first = false;
     t = u.start + i1;
   }
@@ -602,90 +613,114 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
 
 // Merges the partials of units cut by a range boundary:
 //   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w.
-// One work-group per (unit, 32-feature slice); thread = query row.  The
-// contributing slots are found once per work-group, then every partial load
-// is independent (coalesced across rows).
-constexpr int kMaxContrib = 1024;
+// One single-wave work-group per (unit, 16-feature slice, 64-row chunk);
+// thread = query row.  Contributors are the work-groups whose ranges meet
+// the unit's real tiles, w_lo .. w_hi; each left its partial in slot 2w, or
+// 2w + 1 for w_lo when its range began inside an earlier unit.  Four
+// contributors are read per step to keep enough loads in flight.
+constexpr int kCombineRows = 64;
+constexpr int kCombineFeat = 16;
+constexpr int kCombineUnroll = 4;
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(Params p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int scan[kCombineThreads];
-  __shared__ int slots[kMaxContrib];
-  int *pre = (int *)smem;
-  build_prefix<kCombineThreads>(p, pre, scan);
+__global__ __launch_bounds__(kCombineRows) void attn_combine_kernel(Params p) {
   const int upb = p.Hkv * p.qchunks;
   const int uid = blockIdx.x;
   const int b = uid / upb, ui = uid % upb;
   const int h = ui / p.qchunks, qc = ui % p.qchunks;
-  const int T = seq_tiles(seq_len(p, b));
-  const int us = pre[b] + ui * T, ue = us + T;
-  const int total = pre[p.B];
+  const int pb = p.ws_pre[b];
+  const int T = (p.ws_pre[b + 1] - pb) / upb;
+  const int total = p.ws_pre[p.B];
+  const int nreal = T - kUnitPad;
+  const int us = pb + ui * T;
   const int R = (total + p.G - 1) / p.G;
-  const int w_lo = us / R, w_hi = (ue - 1) / R;
+  const int w_lo = us / R, w_hi = (us + nreal - 1) / R;
   if (w_lo == w_hi) return;  // finished in place by one work-group
-  const int n = w_hi - w_lo + 1;
-  for (int k = threadIdx.x; k < n; k += kCombineThreads) {
-    const int w = w_lo + k;
-    slots[k] = 2 * w + (locate(p, pre, w * R).id == uid ? 0 : 1);
-  }
-  __syncthreads();
-  const int qloc = threadIdx.x;
+  const int qloc = blockIdx.z * kCombineRows + threadIdx.x;
   const int qi = qc * kQRows + qloc;
   if (qi >= p.S * p.g) return;
+  const int lo_slot = 2 * w_lo + (w_lo * R != us ? 1 : 0);
+  auto slot_of = [&](int w) { return w == w_lo ? lo_slot : 2 * w; };
 
   float M = -INFINITY;
-  for (int k = 0; k < n; ++k) M = fmaxf(M, p.ws_ml[((size_t)slots[k] * kQRows + qloc) * 2]);
+  for (int w = w_lo; w <= w_hi; ++w) M = fmaxf(M, p.ws_ml[((size_t)slot_of(w) * kQRows + qloc) * 2]);
+
+  // features f0 .. f0+15 of this row: 16-byte pieces at accumulator block
+  // db = f0/32, register groups r4 = (f0%32)/8 + {0, 1}, lane halves hh = 0, 1
+  const int f0 = kCombineFeat * blockIdx.y;
+  const int db = f0 / 32, r40 = (f0 % 32) / 8;
+  constexpr int WROWS = 32 * kQB;
+  const int wv = qloc / WROWS, qb = (qloc % WROWS) / 32, ln = qloc % 32;
+  const size_t base = (((size_t)(wv * kQB + qb) * (D / 32) + db) * 4 + r40) * 64 + ln;
+  float acc[kCombineFeat];
+#pragma unroll
+  for (int e = 0; e < kCombineFeat; ++e) acc[e] = 0.f;
   float lt = 0.f;
-  for (int k = 0; k < n; ++k) {
-    const float *m = p.ws_ml + ((size_t)slots[k] * kQRows + qloc) * 2;
-    lt += __builtin_amdgcn_exp2f(m[0] - M) * m[1];
+  for (int w0 = w_lo; w0 <= w_hi; w0 += kCombineUnroll) {
+    f32x4 x[kCombineUnroll][4];
+    float mw[kCombineUnroll], lw[kCombineUnroll];
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      const int w = min(w0 + k, w_hi);
+      const int slot = slot_of(w);
+      const float *m = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
+      mw[k] = m[0];
+      lw[k] = m[1];
+      const f32x4 *src = (const f32x4 *)(p.ws_o + (size_t)slot * D * kQRows) + base;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) x[k][2 * r + hh] = src[r * 64 + hh * 32];
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      if (w0 + k > w_hi) break;
+      const float wt = __builtin_amdgcn_exp2f(mw[k] - M);
+      lt += wt * lw[k];
+      // x[k][2*r + hh][e] is feature f0 + 8*r + 4*hh + e
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[8 * r + 4 * hh + e] += wt * x[k][2 * r + hh][e];
+    }
   }
   const float inv = 1.f / lt;
-  const int d0 = 32 * blockIdx.y;
-  float acc[32];
-#pragma unroll
-  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
-  for (int k = 0; k < n; ++k) {
-    const float wt = __builtin_amdgcn_exp2f(p.ws_ml[((size_t)slots[k] * kQRows + qloc) * 2] - M) * inv;
-    const float *src = p.ws_o + ((size_t)slots[k] * D + d0) * kQRows + qloc;
-    float x[32];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) x[e] = src[(size_t)e * kQRows];
-#pragma unroll
-    for (int e = 0; e < 32; ++e) acc[e] += wt * x[e];
-  }
   const int t = qi / p.g, j = qi % p.g;
-  __bf16 *dst = p.out + (((size_t)b * p.S + t) * p.Hq + h * p.g + j) * D + d0;
+  __bf16 *dst = p.out + (((size_t)b * p.S + t) * p.Hq + h * p.g + j) * D + f0;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    f32x8 v = {acc[8 * c + 0], acc[8 * c + 1], acc[8 * c + 2], acc[8 * c + 3],
-               acc[8 * c + 4], acc[8 * c + 5], acc[8 * c + 6], acc[8 * c + 7]};
+  for (int c = 0; c < 2; ++c) {
+    f32x8 v = {acc[8 * c + 0] * inv, acc[8 * c + 1] * inv, acc[8 * c + 2] * inv, acc[8 * c + 3] * inv,
+               acc[8 * c + 4] * inv, acc[8 * c + 5] * inv, acc[8 * c + 6] * inv, acc[8 * c + 7] * inv};
     *(bf16x8 *)(dst + 8 * c) = __builtin_convertvector(v, bf16x8);
   }
 }
 
 template <int D>
 hipError_t launch_d(const Params &prm, hipStream_t stream) {
-  const size_t pre_bytes = (size_t)(prm.B + 1) * sizeof(int);
+  const size_t pre_bytes = (size_t)(2 * prm.B + 1) * sizeof(int);   // pre[] and lens[]
   const size_t split_lds = Geo<D>::RING_BYTES + kPageCache * sizeof(int) + pre_bytes;
   static bool attr_done = false;   // benign race: every caller sets the same value
   if (!attr_done) {
     const hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<D>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)(Geo<D>::RING_BYTES + kPageCache * sizeof(int) +
-                                                   (kMaxBatch + 1) * sizeof(int)));
+                                                   (2 * kMaxBatch + 1) * sizeof(int)));
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   hipLaunchKernelGGL(attn_split_kernel<D>, dim3(prm.G), dim3(kThreads), split_lds, stream, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(prm.B * prm.Hkv * prm.qchunks, D / 32),
-                     dim3(kCombineThreads),
-                     pre_bytes, stream, prm);
+  hipLaunchKernelGGL(attn_combine_kernel<D>,
+                     dim3(prm.B * prm.Hkv * prm.qchunks, D / kCombineFeat, kQRows / kCombineRows),
+                     dim3(kCombineRows), 0, stream, prm);
   return hipGetLastError();
 }
+
+// bytes of the published prefix at the head of the workspace (256-aligned)
+size_t ws_pre_bytes(int B) { return (((size_t)(B + 1) * sizeof(int)) + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -698,13 +733,13 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus) {
   p.qchunks = (p.S * p.g + kQRows - 1) / kQRows;
   const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)p.D);
   p.scale_log2 = scale * 1.4426950408889634f;
-  const long tiles = (long)p.B * p.Hkv * p.qchunks * ((p.max_ctx + kTile - 1) / kTile + 1);
+  const long tiles = (long)p.B * p.Hkv * p.qchunks * ((p.max_ctx + kTile - 1) / kTile + 1 + kUnitPad);
   long G = (tiles + kMinTiles - 1) / kMinTiles;
   if (G > cus) G = cus;
   if (G > 1024) G = 1024;  // the combine keeps one slot id per contributor in LDS
   if (G < 1) G = 1;
   p.G = (int)G;
-  p.ws_bytes = (size_t)2 * G * ((size_t)p.D * kQRows + 2 * kQRows) * sizeof(float);
+  p.ws_bytes = ws_pre_bytes(p.B) + (size_t)2 * G * ((size_t)p.D * kQRows + 2 * kQRows) * sizeof(float);
   return p;
 }
 
@@ -717,7 +752,8 @@ hipError_t launch_attn_bf16(const AttnPlan &pl, const void *q, const void *k_blk
   prm.k_pages = (const __bf16 *)k_pages; prm.v_pages = (const __bf16 *)v_pages;
   prm.page_table = page_table; prm.ctx_lens = ctx_lens;
   prm.out = (__bf16 *)out;
-  prm.ws_o = (float *)workspace;
+  prm.ws_pre = (int *)workspace;
+  prm.ws_o = (float *)((unsigned char *)workspace + ws_pre_bytes(pl.B));
   prm.ws_ml = prm.ws_o + (size_t)2 * pl.G * pl.D * kQRows;
   prm.B = pl.B; prm.S = pl.S; prm.Hq = pl.Hq; prm.Hkv = pl.Hkv; prm.g = pl.g;
   prm.page_size = pl.page_size; prm.lps = __builtin_ctz((unsigned)pl.page_size);

@@ -16,7 +16,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Largest batch the attention planner keeps in LDS (per-sequence prefix sums).
-constexpr int kMaxBatch = 4096;
+constexpr int kMaxBatch = 2048;
 
 // Shape and launch plan of one bf16 block-attention call.
 struct AttnPlan {
