@@ -64,6 +64,77 @@ def read_traffic(bytes_alg):
     return rec.get("hbm_bytes_per_launch")
 
 
+CALIB_BYTES = 256 << 20
+ATTN_KERNELS = ("attn_split_kernel", "attn_combine_kernel")
+
+
+def _read_counters(path, counter):
+    """Mean per-dispatch value of `counter` per kernel family from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            if "attn_split_kernel" in name:
+                key = "attn_split_kernel"
+            elif "attn_combine_kernel" in name:
+                key = "attn_combine_kernel"
+            elif "direct_copy" in name or "copyBuffer" in name:
+                key = "copy"
+            else:
+                continue
+            per.setdefault(key, []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_pmc(fetch_csv, write_csv, out_md):
+    fetch = _read_counters(fetch_csv, "FETCH_SIZE")
+    write = _read_counters(write_csv, "WRITE_SIZE")
+    # the calibration copy is the largest copy dispatch
+    cf, cw = max(fetch["copy"]), max(write["copy"])
+    kib = CALIB_BYTES / 1024.0
+    sf, sw = kib / cf, kib / cw
+    rec = {"source_hash": attn_source_hash(), "fetch_scale": sf, "write_scale": sw}
+    lines = ["# Attention HBM traffic counters (config-5 layer launch)", "",
+             "Counters from two `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per",
+             "dispatch) over `python3 bench.py --only-attn`, scaled by the same counter on a plain",
+             "256 MiB device copy (fetch scale %.4f, write scale %.4f)." % (sf, sw), "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |",
+             "|---|---|---|---|---|"]
+    total = 0.0
+    for k in ATTN_KERNELS:
+        f = sum(fetch.get(k, [0])) / max(len(fetch.get(k, [])), 1)
+        w = sum(write.get(k, [0])) / max(len(write.get(k, [])), 1)
+        b = (f * sf + w * sw) * 1024.0
+        total += b
+        lines.append("| %s | %d | %.0f | %.0f | %.3e |" % (k, len(fetch.get(k, [])), f, w, b))
+        rec[k] = {"fetch_kib": f, "write_kib": w, "bytes": b}
+    rec["hbm_bytes_per_launch"] = total
+    lines += ["", "HBM bytes per tt_block_attn launch (split + combine): %.4e" % total, "",
+              "COUNTERS_JSON " + json.dumps(rec)]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_stats(stats_csv, out_md):
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
+             "| kernel | calls | avg us | total % |", "|---|---|---|---|"]
+    for r in rows[:12]:
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "").replace("tt::(anonymous namespace)::", "")
+        lines.append("| %s | %s | %.2f | %.2f |" % (short[:80], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                   float(r["Percentage"])))
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,8 +143,19 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-iters", type=int, default=96, help="launches in the attention-only timing")
-    ap.add_argument("--only-attn", action="store_true", help="profiling aid: attention launches only")
+    ap.add_argument("--only-attn", action="store_true",
+                    help="counter runs: attention launches plus one 256 MiB calibration copy")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files into a summary")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="turn a rocprofv3 --stats kernel_stats.csv into a summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -209,6 +291,13 @@ def main():
     un_gbs = B * S * V * 4 / un_s / 1e9
     log("unmask: %.1f us/call, %.0f GB/s" % (un_s * 1e6, un_gbs))
     if args.only_attn:
+        # calibration for FETCH_SIZE / WRITE_SIZE: a plain device copy of 256 MiB
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("attention algorithmic bytes per launch: %d" % attn_bytes)
         return
 
     # ---- CPU oracle on a bounded sample of the same workload

@@ -9,15 +9,20 @@
 //
 // Work decomposition.  A *unit* is (sequence b, KV head h, query chunk of up
 // to 256 rows).  A unit's keys are cut into 64-token *tiles*: ceil(L_b/64)
-// context tiles followed by one tile holding the S block tokens.  All tiles of
-// all units form one flat list; work-group w of G takes the contiguous range
-// [w*R, (w+1)*R), R = ceil(total/G).  Units wholly inside a range are finished
-// in place; a unit cut by a range boundary leaves an unnormalised fp32 partial
-// (O^T, running max, running sum) in one of the work-group's two workspace
-// slots, and the combine kernel merges those partials.  Each block token is
-// therefore seen exactly once, and no work-group holds more than two
-// partials.  The plan is rebuilt on the device from ctx_lens, so the host
-// never needs the lengths.
+// context tiles, one tile holding the S block tokens, then kUnitPad virtual
+// tiles that only stand for the unit's fixed cost.  All tiles of all units
+// form one flat list; work-group w of G takes the contiguous range
+// [w*R, (w+1)*R), R = ceil(total/G).  Units wholly inside a range are
+// finished in place; a unit cut by a range boundary leaves a partial
+// (O^T / l in bf16, running max and running sum l in fp32) in one of the
+// work-group's two workspace slots, and the combine kernel merges those
+// partials.  Each block token is therefore seen exactly once.  The plan is
+// rebuilt on the device from ctx_lens, so the host never needs the lengths.
+//
+// Waves are split into a lead and a lag group sharing the SIMDs: the lag
+// group runs one pipeline stage behind (P.V of the previous tile first), so
+// the two waves on a SIMD are in different phases and one's softmax VALU
+// work overlaps the other's MFMAs.
 //
 // Per work-group: 8 waves, 32 query rows each.  Context tiles stream from HBM
 // straight into a ring of kStages LDS buffers with global_load_lds_dwordx4
@@ -75,8 +80,8 @@ struct Params {
   const int32_t *page_table, *ctx_lens;
   __bf16 *out;
   int *ws_pre;   // [B+1] flat-tile prefix, published for the combine
-  float *ws_o;   // [2G][D*256] unnormalised O^T partials
-  float *ws_ml;  // [2G][256][2]  (reference max in log2 units, sum)
+  __bf16 *ws_o; // [2G][D*256] partial O^T / l (bf16)
+  float *ws_ml;  // [2G][256][2]  (reference max in log2 units, sum l)
   int B, S, Hq, Hkv, g, page_size, lps, max_pages, num_pages, max_ctx, qchunks, G;
   float sl2;
 };
@@ -323,36 +328,69 @@ struct PTile {
   bf16x8 v[2][kQB][2];  // probabilities of a 64-key tile as P.V B-operands
 };
 
-// Scores and online softmax of one 64-key tile from `stage`.  The key
-// operands of each 32-key half are read from LDS before its score MFMAs
-// (sched_barrier keeps the compiler from sinking the reads next to their
-// uses, which would expose the LDS latency once per MFMA).  Rescales the accumulators when the running
-// max grows by more than 2^kLazy, then returns P rounded to bf16.
+// MFMA A-operands of one 32-key half of a tile: keys (score MFMAs) or
+// values (P.V MFMAs).  Loaded from LDS one phase ahead of their use.
 template <int D>
-__device__ __forceinline__ void scores_softmax(const Params &p, const unsigned char *stage,
-                                               int nvalid, const bf16x8 (&qr)[kQB][Geo<D>::KS],
-                                               Acc<D> &A, PTile<D> &P) {
-  using G = Geo<D>;
+struct KOps {
+  bf16x8 v[Geo<D>::KS];
+};
+template <int D>
+struct VOps {
+  bf16x8 v[2][Geo<D>::DB];
+};
+
+template <int D>
+__device__ __forceinline__ void load_k(const unsigned char *stage, int tb, KOps<D> &k) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31, hl = lane >> 5;
-  const unsigned char *Ks = stage;
+#pragma unroll
+  for (int ks = 0; ks < Geo<D>::KS; ++ks)
+    k.v[ks] = *(const bf16x8 *)(stage + k_off<D>(32 * tb + ln, 2 * ks + hl));
+}
 
-  f32x16 s[2][kQB];
+template <int D>
+__device__ __forceinline__ void load_v(const unsigned char *stage, int tb, VOps<D> &v) {
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31, hl = lane >> 5;
+  const unsigned char *Vs = stage + Geo<D>::K_BYTES;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    bf16x8 ka[G::KS];
+  for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks)
-      ka[ks] = *(const bf16x8 *)(Ks + k_off<D>(32 * tb + ln, 2 * ks + hl));
-    __builtin_amdgcn_sched_barrier(0);
+    for (int db = 0; db < Geo<D>::DB; ++db)
+      v.v[cc][db] = *(const bf16x8 *)(Vs + v_off(32 * db + ln, 4 * tb + 2 * cc + hl));
+}
+
+// S^T for one 32-key half: s[qb] = K_half . Q^T
+template <int D>
+__device__ __forceinline__ void scores_half(const KOps<D> &k, const bf16x8 (&qr)[kQB][Geo<D>::KS],
+                                            f32x16 (&s)[kQB]) {
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) s[tb][qb] = f32x16{};
+  for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks)
+  for (int ks = 0; ks < Geo<D>::KS; ++ks)
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.v[ks], qr[qb][ks], s[qb], 0, 0, 0);
+}
+
+// O^T += V^T . P^T for one 32-key half
+template <int D>
+__device__ __forceinline__ void pv_half(const VOps<D> &v, const PTile<D> &P, int tb, Acc<D> &A) {
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int db = 0; db < Geo<D>::DB; ++db)
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
-        s[tb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qr[qb][ks], s[tb][qb], 0, 0, 0);
-  }
+        A.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.v[cc][db], P.v[tb][qb][cc], A.o[db][qb], 0, 0, 0);
+}
+
+// Online softmax of a tile's scores (log2 domain): rescales the accumulators
+// when the running max grows by more than 2^kLazy, returns P in bf16.
+template <int D>
+__device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2][kQB], int nvalid,
+                                             Acc<D> &A, PTile<D> &P) {
+  const int hl = (threadIdx.x & 63) >> 5;
   // key index of accumulator register r in lane half hl: 32*tb + 16*(r/8) + 8*hl + r%8
   if (nvalid < kTile) {
 #pragma unroll
@@ -381,7 +419,7 @@ __device__ __forceinline__ void scores_softmax(const Params &p, const unsigned c
       if (need) A.mref[qb] = mxs;
       A.lsum[qb] *= f;
 #pragma unroll
-      for (int db = 0; db < G::DB; ++db) A.o[db][qb] *= f;
+      for (int db = 0; db < Geo<D>::DB; ++db) A.o[db][qb] *= f;
     }
     const float nm = -A.mref[qb];
     float acc = 0.f;
@@ -402,31 +440,79 @@ __device__ __forceinline__ void scores_softmax(const Params &p, const unsigned c
   }
 }
 
-// O^T += V^T . P^T for one tile; each half's value operands are read before
-// its MFMAs.
+// Lead role, whole tile: scores -> softmax -> P.V.  The first value half is
+// read before the softmax and the second before the first half's P.V MFMAs,
+// so LDS latency hides behind other work.
 template <int D>
-__device__ __forceinline__ void pv_tile(const unsigned char *stage, const PTile<D> &P, Acc<D> &A) {
-  using G = Geo<D>;
-  const int lane = threadIdx.x & 63;
-  const int ln = lane & 31, hl = lane >> 5;
-  const unsigned char *Vs = stage + G::K_BYTES;
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    bf16x8 va[2][G::DB];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-        va[cc][db] = *(const bf16x8 *)(Vs + v_off(32 * db + ln, 4 * tb + 2 * cc + hl));
+__device__ __forceinline__ void tile_lead(const Params &p, const unsigned char *stage, int nvalid,
+                                          const bf16x8 (&qr)[kQB][Geo<D>::KS], Acc<D> &A,
+                                          PTile<D> &P) {
+  f32x16 s[2][kQB];
+  {
+    KOps<D> k;
+    load_k<D>(stage, 0, k);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          A.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][db], P.v[tb][qb][cc], A.o[db][qb], 0, 0, 0);
+    scores_half<D>(k, qr, s[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k<D>(stage, 1, k);
+    __builtin_amdgcn_sched_barrier(0);
+    scores_half<D>(k, qr, s[1]);
   }
+  VOps<D> v;
+  load_v<D>(stage, 0, v);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax_tile<D>(p, s, nvalid, A, P);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_half<D>(v, P, 0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v<D>(stage, 1, v);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_half<D>(v, P, 1, A);
+}
+
+// Lag role: P.V of the previous tile (`prev`, probabilities in P), then
+// scores and softmax of this tile.  (Reading this tile's keys during the
+// P.V MFMAs would need 32 more live registers than the 256 a wave has at
+// two waves per SIMD.)
+template <int D>
+__device__ __forceinline__ void tile_lag(const Params &p, const unsigned char *prev,
+                                         const unsigned char *stage, int nvalid,
+                                         const bf16x8 (&qr)[kQB][Geo<D>::KS], Acc<D> &A,
+                                         PTile<D> &P) {
+  KOps<D> k;
+  if (prev) {
+    VOps<D> v;
+    load_v<D>(prev, 0, v);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_half<D>(v, P, 0, A);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<D>(prev, 1, v);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_half<D>(v, P, 1, A);
+  }
+  load_k<D>(stage, 0, k);
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s[2][kQB];
+  scores_half<D>(k, qr, s[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_k<D>(stage, 1, k);
+  __builtin_amdgcn_sched_barrier(0);
+  scores_half<D>(k, qr, s[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax_tile<D>(p, s, nvalid, A, P);
+}
+
+// P.V of one tile whose probabilities are in P (lag role's last tile).
+template <int D>
+__device__ __forceinline__ void tile_pv(const unsigned char *stage, const PTile<D> &P, Acc<D> &A) {
+  VOps<D> v;
+  load_v<D>(stage, 0, v);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_half<D>(v, P, 0, A);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v<D>(stage, 1, v);
+  __builtin_amdgcn_sched_barrier(0);
+  pv_half<D>(v, P, 1, A);
 }
 
 // Context tiles [i0, ctx_end) of unit u through the LDS ring, in sub-ranges
@@ -465,15 +551,13 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
         lds_barrier();
       }
       if (!LAG) {
-        scores_softmax<D>(p, stage, nvalid, qr, A, P);
-        pv_tile<D>(stage, P, A);
+        tile_lead<D>(p, stage, nvalid, qr, A, P);
       } else {
-        if (prev) pv_tile<D>(prev, P, A);
-        scores_softmax<D>(p, stage, nvalid, qr, A, P);
+        tile_lag<D>(p, prev, stage, nvalid, qr, A, P);
         prev = stage;
       }
     }
-    if (LAG && prev) pv_tile<D>(prev, P, A);
+    if (LAG && prev) tile_pv<D>(prev, P, A);
     lds_barrier();   // ring and page cache free for reuse
   }
 }
@@ -535,8 +619,7 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
     unsigned char *stage = ring;
     stage_block_tile<D>(p, u, stage);
     lds_barrier();
-    scores_softmax<D>(p, stage, p.S, qr, A, P);
-    pv_tile<D>(stage, P, A);
+    tile_lead<D>(p, stage, p.S, qr, A, P);
     lds_barrier();
   }
 
@@ -562,17 +645,19 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
           }
       }
     } else {
-      // partial O^T in accumulator layout: float4 (registers 4*r4 .. 4*r4+3)
-      // of lane l at ((((wave*kQB + qb)*DB + db)*4 + r4)*64 + l); features
-      // 32*db + 8*r4 + 4*(l/32) + 0..3 of query row wave*WROWS + qb*32 + l%32
-      f32x4 *wo = (f32x4 *)(p.ws_o + (size_t)slot * D * kQRows);
+      // partial O^T / l in bf16, accumulator layout: 4 x bf16 (registers
+      // 4*r4 .. 4*r4+3) of lane l at ((((wave*kQB + qb)*DB + db)*4 + r4)*64 + l);
+      // features 32*db + 8*r4 + 4*(l/32) + 0..3 of query row
+      // wave*WROWS + qb*32 + l%32.  Normalising keeps the values in V's range.
+      const float inv = 1.f / ltot;
+      bf16x4 *wo = (bf16x4 *)(p.ws_o + (size_t)slot * D * kQRows);
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 v = {A.o[db][qb][4 * r4], A.o[db][qb][4 * r4 + 1], A.o[db][qb][4 * r4 + 2],
-                           A.o[db][qb][4 * r4 + 3]};
-          wo[(((wave * kQB + qb) * G::DB + db) * 4 + r4) * 64 + lane] = v;
+          const f32x4 v = {A.o[db][qb][4 * r4] * inv, A.o[db][qb][4 * r4 + 1] * inv,
+                           A.o[db][qb][4 * r4 + 2] * inv, A.o[db][qb][4 * r4 + 3] * inv};
+          wo[(((wave * kQB + qb) * G::DB + db) * 4 + r4) * 64 + lane] = __builtin_convertvector(v, bf16x4);
         }
       if (hl == 0) {
         float *wm = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
@@ -612,7 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
 }
 
 // Merges the partials of units cut by a range boundary:
-//   O = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w,  M = max_w m_w.
+//   O = sum_w c_w (O_w / l_w) / sum_w c_w,  c_w = 2^(m_w - M) l_w,  M = max_w m_w.
 // One single-wave work-group per (unit, 16-feature slice, 64-row chunk);
 // thread = query row.  Contributors are the work-groups whose ranges meet
 // the unit's real tiles, w_lo .. w_hi; each left its partial in slot 2w, or
@@ -666,17 +751,18 @@ __global__ __launch_bounds__(kCombineRows) void attn_combine_kernel(Params p) {
       const float *m = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
       mw[k] = m[0];
       lw[k] = m[1];
-      const f32x4 *src = (const f32x4 *)(p.ws_o + (size_t)slot * D * kQRows) + base;
+      const bf16x4 *src = (const bf16x4 *)(p.ws_o + (size_t)slot * D * kQRows) + base;
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) x[k][2 * r + hh] = src[r * 64 + hh * 32];
+        for (int hh = 0; hh < 2; ++hh)
+          x[k][2 * r + hh] = __builtin_convertvector(src[r * 64 + hh * 32], f32x4);
     }
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) {
       if (w0 + k > w_hi) break;
-      const float wt = __builtin_amdgcn_exp2f(mw[k] - M);
-      lt += wt * lw[k];
+      const float wt = __builtin_amdgcn_exp2f(mw[k] - M) * lw[k];   // partials hold O / l
+      lt += wt;
       // x[k][2*r + hh][e] is feature f0 + 8*r + 4*hh + e
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -739,7 +825,7 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus) {
   if (G > 1024) G = 1024;  // the combine keeps one slot id per contributor in LDS
   if (G < 1) G = 1;
   p.G = (int)G;
-  p.ws_bytes = ws_pre_bytes(p.B) + (size_t)2 * G * ((size_t)p.D * kQRows + 2 * kQRows) * sizeof(float);
+  p.ws_bytes = ws_pre_bytes(p.B) + (size_t)2 * G * ((size_t)p.D * kQRows * 2 + 2 * kQRows * sizeof(float));
   return p;
 }
 
@@ -753,8 +839,8 @@ hipError_t launch_attn_bf16(const AttnPlan &pl, const void *q, const void *k_blk
   prm.page_table = page_table; prm.ctx_lens = ctx_lens;
   prm.out = (__bf16 *)out;
   prm.ws_pre = (int *)workspace;
-  prm.ws_o = (float *)((unsigned char *)workspace + ws_pre_bytes(pl.B));
-  prm.ws_ml = prm.ws_o + (size_t)2 * pl.G * pl.D * kQRows;
+  prm.ws_o = (__bf16 *)((unsigned char *)workspace + ws_pre_bytes(pl.B));
+  prm.ws_ml = (float *)(prm.ws_o + (size_t)2 * pl.G * pl.D * kQRows);
   prm.B = pl.B; prm.S = pl.S; prm.Hq = pl.Hq; prm.Hkv = pl.Hkv; prm.g = pl.g;
   prm.page_size = pl.page_size; prm.lps = __builtin_ctz((unsigned)pl.page_size);
   prm.max_pages = pl.max_pages; prm.num_pages = pl.num_pages;
