@@ -42,14 +42,10 @@ namespace {
 
 constexpr int kTile = 64;        // keys per tile
 constexpr int kQRows = 256;      // query rows per unit
-#ifndef TT_ATTN_QB
-#define TT_ATTN_QB 1
-#endif
 #ifndef TT_ATTN_STAGES
 #define TT_ATTN_STAGES 4
 #endif
-constexpr int kQB = TT_ATTN_QB;  // 32-row query blocks per wave
-constexpr int kThreads = 64 * (kQRows / 32) / kQB;  // waves x 64 lanes
+constexpr int kThreads = 64 * (kQRows / 32);  // one wave per 32 query rows
 constexpr int kStages = TT_ATTN_STAGES;  // LDS ring depth (tiles in flight + 1)
 constexpr int kPageCache = 1024; // page ids cached per sub-range
 constexpr int kMinTiles = 8;     // smallest range worth a work-group
@@ -199,59 +195,188 @@ __device__ __forceinline__ void lds_barrier() {
 // vmcnt-only s_waitcnt immediate (gfx9 encoding; expcnt/lgkmcnt left at max).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-// Wait until at most `tiles_after` tiles' worth of direct loads are in flight.
+// Which waves issue the direct loads.  kIssue = 1: every wave issues its own
+// share of a tile; 2: each lead wave w also issues the share of its lag
+// partner w + waves/2, so that the lag waves, which carry the longer compute,
+// never block on a full memory queue.
+#ifndef TT_ATTN_ISSUE
+#define TT_ATTN_ISSUE 2
+#endif
+constexpr int kIssue = TT_ATTN_ISSUE;
+constexpr int kWaves = kThreads / 64;
+static_assert(kIssue == 1 || kIssue == 2, "shares per issuing wave");
+
+// Wait until at most `tiles_after` tiles' worth of this wave's direct loads
+// are in flight.
 template <int D>
 __device__ __forceinline__ void wait_tiles(int tiles_after) {
-  constexpr int L = Geo<D>::LPT;
+  constexpr int L = Geo<D>::LPT * kIssue;
   if (tiles_after <= 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   else if (tiles_after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
   else if (tiles_after == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
   else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * L));
-  static_assert(3 * Geo<D>::LPT < 64, "vmcnt range");
+  static_assert(3 * Geo<D>::LPT * kIssue < 64, "vmcnt range");
   static_assert(kStages <= 4, "wait_tiles covers up to 3 tiles in flight");
 }
 
-// Issue the direct HBM->LDS loads of context tile i into `stage`.  Each wave
-// instruction fills 1 KiB of LDS contiguously (lane l -> bytes 16l..16l+15),
-// so lane l fetches whichever key/value chunk the swizzled layout puts there.
+// Direct-load slots.  Each wave instruction fills 1 KiB of LDS contiguously
+// (lane l -> bytes 16l..16l+15), and lane l fetches whichever key/value chunk
+// the swizzled layout puts there.  An issuing wave iw owns NL = LPT-part *
+// kIssue consecutive KiB of the key part and of the value part of a stage,
+// so that its loads share one LDS base (M0) and differ only in the
+// instruction's immediate offset, which applies to both addresses.
+template <int D>
+struct Share {
+  static constexpr int NK = Geo<D>::KPT * kIssue;  // key loads per issuing wave
+  static constexpr int NV = Geo<D>::VPT * kIssue;  // value loads per issuing wave
+  static_assert(NK <= 4 && NV <= 4, "immediate offsets reach 4 KiB");
+};
+// Token t and chunk c fetched by this lane for key load n of issuing wave iw.
+template <int D>
+__device__ __forceinline__ void key_slot(int iw, int n, int &t, int &c) {
+  using G = Geo<D>;
+  const int slot = (iw * Share<D>::NK + n) * 64 + (threadIdx.x & 63);
+  const int r = slot / G::KCH, s = slot % G::KCH;
+  t = (r & ~31) | pi_row(r & 31);  // token within the tile
+  c = s ^ (r & (G::KCH - 1));      // 16-byte feature chunk
+}
+// Feature row d and 8-token chunk c fetched for value load n.
+template <int D>
+__device__ __forceinline__ void value_slot(int iw, int n, int &d, int &c) {
+  const int slot = (iw * Share<D>::NV + n) * 64 + (threadIdx.x & 63);
+  d = slot >> 3;
+  c = (slot & 7) ^ ((d & 7) ^ ((d >> 3) & 1));
+}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 // Positions past the context are clamped to a valid token: keys there are
 // masked by score, values are zeroed in LDS before use.
+__device__ __forceinline__ int key_pos(const Unit &u, int i, int t) {
+  return min(i * kTile + t, u.L - 1);
+}
+__device__ __forceinline__ int value_pos(const Unit &u, int i, int c) {
+  const int pos0 = i * kTile + 8 * c;
+  return pos0 < u.L ? pos0 : ((u.L - 1) & ~7);
+}
+
+// Page ids behind this lane's direct loads of one tile, read from the LDS
+// page-id cache one tile ahead of their use.  With pages of at least one
+// tile (BIG), a tile lies inside one page: one id per tile, wave-uniform.
+template <int D, bool BIG>
+struct TilePages {
+  int k[Share<D>::NK], v[Share<D>::NV];
+};
 template <int D>
-__device__ __forceinline__ void issue_tile(const Params &p, const Unit &u, int i,
-                                           unsigned char *stage, const int *pcache, int pbase) {
-  using G = Geo<D>;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tok0 = i * kTile;
-  const int pmask = p.page_size - 1;
+struct TilePages<D, true> {
+  int pg;
+};
+
+template <int D, bool BIG>
+__device__ __forceinline__ void read_pages(const Params &p, const Unit &u, int i, const int *pcache,
+                                           int pbase, TilePages<D, BIG> &pg) {
+  if constexpr (BIG) {
+    pg.pg = pcache[((i * kTile) >> p.lps) - pbase];
+  } else {
+    const int iw = wave_id();
 #pragma unroll
-  for (int kk = 0; kk < G::KPT; ++kk) {
-    const int slot = kk * kThreads + tid;
-    const int r = slot / G::KCH, s = slot % G::KCH;
-    const int t = (r & ~31) | pi_row(r & 31);
-    const int c = s ^ (r & (G::KCH - 1));
-    const int pos = min(tok0 + t, u.L - 1);
-    const int pg = pcache[(pos >> p.lps) - pbase];
-    const __bf16 *src =
-        p.k_pages + (((size_t)pg * p.Hkv + u.h) * p.page_size + (pos & pmask)) * D + 8 * c;
-    __builtin_amdgcn_global_load_lds((const void *)src,
-                                     (lds_void *)(stage + (kk * kThreads + wave * 64) * 16), 16, 0,
-                                     0);
-  }
+    for (int n = 0; n < Share<D>::NK; ++n) {
+      int t, c;
+      key_slot<D>(iw, n, t, c);
+      pg.k[n] = pcache[(key_pos(u, i, t) >> p.lps) - pbase];
+    }
 #pragma unroll
-  for (int vv = 0; vv < G::VPT; ++vv) {
-    const int slot = vv * kThreads + tid;
-    const int d = slot >> 3, s = slot & 7;
-    const int c = s ^ ((d & 7) ^ ((d >> 3) & 1));
-    const int pos0 = tok0 + 8 * c;
-    const int pos = pos0 < u.L ? pos0 : ((u.L - 1) & ~7);
-    const int pg = pcache[(pos >> p.lps) - pbase];
-    const __bf16 *src = p.v_pages + (((size_t)pg * p.Hkv + u.h) * D + d) * p.page_size + (pos & pmask);
-    __builtin_amdgcn_global_load_lds(
-        (const void *)src, (lds_void *)(stage + G::K_BYTES + (vv * kThreads + wave * 64) * 16), 16,
-        0, 0);
+    for (int n = 0; n < Share<D>::NV; ++n) {
+      int d, c;
+      value_slot<D>(iw, n, d, c);
+      pg.v[n] = pcache[(value_pos(u, i, c) >> p.lps) - pbase];
+    }
   }
 }
+
+// One direct load: global `src` -> LDS lds + n KiB (+ 16 * lane).  The
+// immediate offset n KiB is added by the hardware to both addresses.
+__device__ __forceinline__ void dma(const __bf16 *src, unsigned char *lds, int n) {
+  const unsigned char *g = (const unsigned char *)src;
+  switch (n) {
+    case 0: __builtin_amdgcn_global_load_lds((const void *)g, (lds_void *)lds, 16, 0, 0); break;
+    case 1: __builtin_amdgcn_global_load_lds((const void *)(g - 1024), (lds_void *)lds, 16, 1024, 0); break;
+    case 2: __builtin_amdgcn_global_load_lds((const void *)(g - 2048), (lds_void *)lds, 16, 2048, 0); break;
+    default: __builtin_amdgcn_global_load_lds((const void *)(g - 3072), (lds_void *)lds, 16, 3072, 0); break;
+  }
+}
+
+// Issue this wave's direct HBM->LDS loads of context tile i into `stage`.
+// BIG: the tile's 64 tokens sit in one page, so the page base is scalar and
+// each lane adds a fixed offset; positions past the context stay inside that
+// page (masked keys, values zeroed in LDS).  Otherwise positions are clamped
+// to the context and every lane looks up its own page.
+template <int D, bool BIG>
+__device__ __forceinline__ void issue_tile(const Params &p, const Unit &u, int i,
+                                           unsigned char *stage, const TilePages<D, BIG> &pg) {
+  using G = Geo<D>;
+  const int iw = wave_id();
+  const int pmask = p.page_size - 1;
+  unsigned char *kl = stage + iw * Share<D>::NK * 1024;
+  unsigned char *vl = stage + G::K_BYTES + iw * Share<D>::NV * 1024;
+  if constexpr (BIG) {
+    const int page = __builtin_amdgcn_readfirstlane(pg.pg);
+    const size_t block = ((size_t)page * p.Hkv + u.h) * p.page_size * D;  // (page, head) block
+    const int off = (i * kTile) & pmask;                                   // tile start in the page
+    const __bf16 *kb = p.k_pages + block + (size_t)off * D;
+    const __bf16 *vb = p.v_pages + block + off;
+#pragma unroll
+    for (int n = 0; n < Share<D>::NK; ++n) {
+      int t, c;
+      key_slot<D>(iw, n, t, c);
+      dma(kb + (unsigned)(t * D + 8 * c), kl, n);
+    }
+#pragma unroll
+    for (int n = 0; n < Share<D>::NV; ++n) {
+      int d, c;
+      value_slot<D>(iw, n, d, c);
+      dma(vb + (unsigned)(d * p.page_size + 8 * c), vl, n);
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < Share<D>::NK; ++n) {
+      int t, c;
+      key_slot<D>(iw, n, t, c);
+      const int pos = key_pos(u, i, t);
+      dma(p.k_pages + (((size_t)pg.k[n] * p.Hkv + u.h) * p.page_size + (pos & pmask)) * D + 8 * c,
+          kl, n);
+    }
+#pragma unroll
+    for (int n = 0; n < Share<D>::NV; ++n) {
+      int d, c;
+      value_slot<D>(iw, n, d, c);
+      const int pos = value_pos(u, i, c);
+      dma(p.v_pages + (((size_t)pg.v[n] * p.Hkv + u.h) * D + d) * p.page_size + (pos & pmask), vl, n);
+    }
+  }
+}
+
+// The direct loads of one tile, issued at the start of an earlier tile's
+// compute, followed by the page-id reads of the tile after it (awaited with
+// the first operand batch).
+template <int D, bool BIG>
+struct TileLoads {
+  const Params &p;
+  const Unit &u;
+  int i;                    // tile to load
+  unsigned char *stage;     // its ring stage
+  TilePages<D, BIG> &pg;    // its page ids; then those of tile i + 1
+  const int *pcache;
+  int pbase, c1;            // page-cache base, end of the sub-range
+  __device__ __forceinline__ void issue() const {
+    if (i >= c1) return;
+    issue_tile<D, BIG>(p, u, i, stage, pg);
+    if (i + 1 < c1) read_pages<D, BIG>(p, u, i + 1, pcache, pbase, pg);
+  }
+};
+
+// No loads (block tile).
+struct NoLoads {
+  __device__ __forceinline__ void issue() const {}
+};
 
 // Zero the value columns of tokens >= nvalid in a landed tile.
 template <int D>
@@ -319,208 +444,238 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 template <int D>
 struct Acc {
-  f32x16 o[Geo<D>::DB][kQB];
-  float mref[kQB], lsum[kQB];
+  f32x16 o[Geo<D>::DB];  // O^T, 32 features x 32 query rows per block
+  float mref, lsum;      // reference max (log2 units), running sum
 };
 
 template <int D>
 struct PTile {
-  bf16x8 v[2][kQB][2];  // probabilities of a 64-key tile as P.V B-operands
+  bf16x8 v[2][2];  // probabilities of a 64-key tile as P.V B-operands [32-key half][16-key chunk]
 };
 
-// MFMA A-operands of one 32-key half of a tile: keys (score MFMAs) or
-// values (P.V MFMAs).  Loaded from LDS one phase ahead of their use.
-template <int D>
-struct KOps {
-  bf16x8 v[Geo<D>::KS];
-};
-template <int D>
-struct VOps {
-  bf16x8 v[2][Geo<D>::DB];
+// Four MFMA A-operands read from LDS together.  A tile's score phase reads
+// 2*KS key operands and its P.V phase 4*DB value operands, four per batch.
+// Two batch buffers alternate: batch n+1 is read while batch n feeds the
+// MFMAs.  Both phase lengths are even, so a phase's first batch always sits
+// in buffer 0 and can be read during the previous phase.
+struct Batch {
+  bf16x8 v[4];
 };
 
 template <int D>
-__device__ __forceinline__ void load_k(const unsigned char *stage, int tb, KOps<D> &k) {
+struct Phases {
+  static constexpr int NQ = 2 * Geo<D>::KS / 4;  // score batches per tile
+  static constexpr int NV = Geo<D>::DB;          // P.V batches per tile
+  static_assert(NQ % 2 == 0 && NV % 2 == 0, "phases must hold an even number of batches");
+};
+
+// Completes this wave's outstanding LDS reads.  While direct-to-LDS loads
+// are in flight the compiler treats LDS read completion as unordered and
+// waits for all of them before a use; waiting here, before the next batch
+// is issued, keeps exactly one batch in flight behind the MFMAs.
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(lgkm0_imm()); }
+
+// Keeps the compiler from moving instructions across phase boundaries.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Score operand e of batch b, j = 4b + e: key half tb = j % 2, k-step
+// ks = j / 2 (the two halves' accumulation chains interleave).
+template <int D>
+__device__ __forceinline__ void read_qk(const unsigned char *stage, int b, Batch &x) {
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31, hl = lane >> 5;
 #pragma unroll
-  for (int ks = 0; ks < Geo<D>::KS; ++ks)
-    k.v[ks] = *(const bf16x8 *)(stage + k_off<D>(32 * tb + ln, 2 * ks + hl));
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * b + e, tb = j & 1, ks = j >> 1;
+    x.v[e] = *(const bf16x8 *)(stage + k_off<D>(32 * tb + ln, 2 * ks + hl));
+  }
 }
 
+// S^T (two 32-key halves) += K . Q^T for batch b
 template <int D>
-__device__ __forceinline__ void load_v(const unsigned char *stage, int tb, VOps<D> &v) {
+__device__ __forceinline__ void mfma_qk(const Batch &x, int b, const bf16x8 (&qr)[Geo<D>::KS],
+                                        f32x16 (&s)[2]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * b + e, tb = j & 1, ks = j >> 1;
+    s[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x.v[e], qr[ks], s[tb], 0, 0, 0);
+  }
+}
+
+// P.V operand e of batch b, j = 4b + e = (2*tb + cc)*DB + db: feature block
+// db, 16-key chunk cc of key half tb.
+template <int D>
+__device__ __forceinline__ void read_pv(const unsigned char *stage, int b, Batch &x) {
+  constexpr int DB = Geo<D>::DB;
   const int lane = threadIdx.x & 63;
   const int ln = lane & 31, hl = lane >> 5;
   const unsigned char *Vs = stage + Geo<D>::K_BYTES;
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-    for (int db = 0; db < Geo<D>::DB; ++db)
-      v.v[cc][db] = *(const bf16x8 *)(Vs + v_off(32 * db + ln, 4 * tb + 2 * cc + hl));
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * b + e, db = j % DB, tc = j / DB;
+    x.v[e] = *(const bf16x8 *)(Vs + v_off(32 * db + ln, 2 * tc + hl));
+  }
 }
 
-// S^T for one 32-key half: s[qb] = K_half . Q^T
+// O^T += V^T . P^T for batch b
 template <int D>
-__device__ __forceinline__ void scores_half(const KOps<D> &k, const bf16x8 (&qr)[kQB][Geo<D>::KS],
-                                            f32x16 (&s)[kQB]) {
+__device__ __forceinline__ void mfma_pv(const Batch &x, int b, const PTile<D> &P, Acc<D> &A) {
+  constexpr int DB = Geo<D>::DB;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) s[qb] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < Geo<D>::KS; ++ks)
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k.v[ks], qr[qb][ks], s[qb], 0, 0, 0);
-}
-
-// O^T += V^T . P^T for one 32-key half
-template <int D>
-__device__ __forceinline__ void pv_half(const VOps<D> &v, const PTile<D> &P, int tb, Acc<D> &A) {
-#pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-    for (int db = 0; db < Geo<D>::DB; ++db)
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-        A.o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.v[cc][db], P.v[tb][qb][cc], A.o[db][qb], 0, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+    const int j = 4 * b + e, db = j % DB, tc = j / DB;
+    A.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x.v[e], P.v[tc >> 1][tc & 1], A.o[db], 0, 0, 0);
+  }
 }
 
 // Online softmax of a tile's scores (log2 domain): rescales the accumulators
 // when the running max grows by more than 2^kLazy, returns P in bf16.
 template <int D>
-__device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2][kQB], int nvalid,
+__device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2], int nvalid,
                                              Acc<D> &A, PTile<D> &P) {
   const int hl = (threadIdx.x & 63) >> 5;
-  // key index of accumulator register r in lane half hl: 32*tb + 16*(r/8) + 8*hl + r%8
+  // key of register r of half tb in lane half hl: 32*tb + 16*(r/8) + 8*hl + r%8
   if (nvalid < kTile) {
+    const int lim = nvalid - 8 * hl;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * tb + 16 * (r >> 3) + 8 * hl + (r & 7);
-        if (key >= nvalid) {
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb) s[tb][qb][r] = -INFINITY;
-        }
-      }
+      for (int r = 0; r < 16; ++r)
+        if (32 * tb + 16 * (r >> 3) + (r & 7) >= lim) s[tb][r] = -INFINITY;
   }
+  float mx = -INFINITY;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    float mx = -INFINITY;
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tb][r]);
+  mx = pair_max(mx);
+  const float mxs = mx * p.sl2;
+  const bool need = mxs > A.mref + kLazy;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float f = need ? __builtin_amdgcn_exp2f(A.mref - mxs) : 1.f;
+    if (need) A.mref = mxs;
+    A.lsum *= f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tb][qb][r]);
-    mx = pair_max(mx);
-    const float mxs = mx * p.sl2;
-    const bool need = mxs > A.mref[qb] + kLazy;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float f = need ? __builtin_amdgcn_exp2f(A.mref[qb] - mxs) : 1.f;
-      if (need) A.mref[qb] = mxs;
-      A.lsum[qb] *= f;
+    for (int db = 0; db < Geo<D>::DB; ++db) A.o[db] *= f;
+  }
+  const float nm = -A.mref;
+  float acc = 0.f;
 #pragma unroll
-      for (int db = 0; db < Geo<D>::DB; ++db) A.o[db][qb] *= f;
+  for (int tb = 0; tb < 2; ++tb) {
+    f32x16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][r], p.sl2, nm));
+      acc += e[r];
     }
-    const float nm = -A.mref[qb];
-    float acc = 0.f;
+    const f32x8 lo = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
+    const f32x8 hi = {e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]};
+    P.v[tb][0] = __builtin_convertvector(lo, bf16x8);
+    P.v[tb][1] = __builtin_convertvector(hi, bf16x8);
+  }
+  A.lsum += acc;
+}
+
+// Score phase of a tile.  Expects its batch 0 in buf[0] (issued, not
+// awaited).  With NEXT_V, issues P.V batch 0 of the same tile into buf[0]
+// under the last score MFMAs.
+template <int D, bool NEXT_V>
+__device__ __forceinline__ void score_phase(const unsigned char *stage,
+                                            const bf16x8 (&qr)[Geo<D>::KS], f32x16 (&s)[2],
+                                            Batch (&buf)[2]) {
+  constexpr int NQ = Phases<D>::NQ;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      f32x16 e;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][qb][r], p.sl2, nm));
-        acc += e[r];
-      }
-      f32x8 lo = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
-      f32x8 hi = {e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]};
-      P.v[tb][qb][0] = __builtin_convertvector(lo, bf16x8);
-      P.v[tb][qb][1] = __builtin_convertvector(hi, bf16x8);
-    }
-    A.lsum[qb] += acc;
+  for (int b = 0; b < NQ; ++b) {
+    lds_wait();
+    sched_fence();
+    if (b + 1 < NQ) read_qk<D>(stage, b + 1, buf[(b + 1) & 1]);
+    else if (NEXT_V) read_pv<D>(stage, 0, buf[0]);
+    sched_fence();
+    mfma_qk<D>(buf[b & 1], b, qr, s);
+    sched_fence();
   }
 }
 
-// Lead role, whole tile: scores -> softmax -> P.V.  The first value half is
-// read before the softmax and the second before the first half's P.V MFMAs,
-// so LDS latency hides behind other work.
-template <int D>
+// P.V phase of a tile whose probabilities are in P.  Expects its batch 0 in
+// buf[0] (issued; complete already if READY).  With NEXT_K, issues score
+// batch 0 of `kstage` into buf[0] under the last P.V MFMAs.
+template <int D, bool READY, bool NEXT_K>
+__device__ __forceinline__ void pv_phase(const unsigned char *stage, const unsigned char *kstage,
+                                         const PTile<D> &P, Acc<D> &A, Batch (&buf)[2]) {
+  constexpr int NV = Phases<D>::NV;
+#pragma unroll
+  for (int b = 0; b < NV; ++b) {
+    if (b > 0 || !READY) lds_wait();
+    sched_fence();
+    if (b + 1 < NV) read_pv<D>(stage, b + 1, buf[(b + 1) & 1]);
+    else if (NEXT_K) read_qk<D>(kstage, 0, buf[0]);
+    sched_fence();
+    mfma_pv<D>(buf[b & 1], b, P, A);
+    sched_fence();
+  }
+}
+
+// Lead role, whole tile: scores -> softmax -> P.V.  The first value batch is
+// read under the last score MFMAs and lands during the softmax.
+template <int D, typename Loads>
 __device__ __forceinline__ void tile_lead(const Params &p, const unsigned char *stage, int nvalid,
-                                          const bf16x8 (&qr)[kQB][Geo<D>::KS], Acc<D> &A,
-                                          PTile<D> &P) {
-  f32x16 s[2][kQB];
-  {
-    KOps<D> k;
-    load_k<D>(stage, 0, k);
-    __builtin_amdgcn_sched_barrier(0);
-    scores_half<D>(k, qr, s[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k<D>(stage, 1, k);
-    __builtin_amdgcn_sched_barrier(0);
-    scores_half<D>(k, qr, s[1]);
-  }
-  VOps<D> v;
-  load_v<D>(stage, 0, v);
-  __builtin_amdgcn_sched_barrier(0);
+                                          const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
+                                          PTile<D> &P, const Loads &ld) {
+  Batch buf[2];
+  f32x16 s[2];
+  ld.issue();
+  read_qk<D>(stage, 0, buf[0]);
+  score_phase<D, true>(stage, qr, s, buf);
   softmax_tile<D>(p, s, nvalid, A, P);
-  __builtin_amdgcn_sched_barrier(0);
-  pv_half<D>(v, P, 0, A);
-  __builtin_amdgcn_sched_barrier(0);
-  load_v<D>(stage, 1, v);
-  __builtin_amdgcn_sched_barrier(0);
-  pv_half<D>(v, P, 1, A);
+  sched_fence();
+  pv_phase<D, false, false>(stage, nullptr, P, A, buf);
 }
 
-// Lag role: P.V of the previous tile (`prev`, probabilities in P), then
-// scores and softmax of this tile.  (Reading this tile's keys during the
-// P.V MFMAs would need 32 more live registers than the 256 a wave has at
-// two waves per SIMD.)
-template <int D>
+// Lag role: P.V of the previous tile (`prev`, probabilities in P, value
+// batch 0 in buf[0], complete), then scores and softmax of this tile; the
+// value batch 0 of this tile is read under the last score MFMAs, for the
+// next call.  FIRST: no previous tile.
+template <int D, bool FIRST, typename Loads>
 __device__ __forceinline__ void tile_lag(const Params &p, const unsigned char *prev,
                                          const unsigned char *stage, int nvalid,
-                                         const bf16x8 (&qr)[kQB][Geo<D>::KS], Acc<D> &A,
-                                         PTile<D> &P) {
-  KOps<D> k;
-  if (prev) {
-    VOps<D> v;
-    load_v<D>(prev, 0, v);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_half<D>(v, P, 0, A);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v<D>(prev, 1, v);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_half<D>(v, P, 1, A);
+                                         const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
+                                         PTile<D> &P, Batch (&buf)[2], const Loads &ld) {
+  f32x16 s[2];
+  ld.issue();
+  if (FIRST) {
+    read_qk<D>(stage, 0, buf[0]);
+  } else {
+    pv_phase<D, true, true>(prev, stage, P, A, buf);
   }
-  load_k<D>(stage, 0, k);
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 s[2][kQB];
-  scores_half<D>(k, qr, s[0]);
-  __builtin_amdgcn_sched_barrier(0);
-  load_k<D>(stage, 1, k);
-  __builtin_amdgcn_sched_barrier(0);
-  scores_half<D>(k, qr, s[1]);
-  __builtin_amdgcn_sched_barrier(0);
+  score_phase<D, true>(stage, qr, s, buf);
   softmax_tile<D>(p, s, nvalid, A, P);
 }
 
-// P.V of one tile whose probabilities are in P (lag role's last tile).
+// Start of context tile i of a sub-range [c0, c1): waits for the tile and
+// zeroes the value tail of a partial tile.  Returns the tile's stage.
 template <int D>
-__device__ __forceinline__ void tile_pv(const unsigned char *stage, const PTile<D> &P, Acc<D> &A) {
-  VOps<D> v;
-  load_v<D>(stage, 0, v);
-  __builtin_amdgcn_sched_barrier(0);
-  pv_half<D>(v, P, 0, A);
-  __builtin_amdgcn_sched_barrier(0);
-  load_v<D>(stage, 1, v);
-  __builtin_amdgcn_sched_barrier(0);
-  pv_half<D>(v, P, 1, A);
+__device__ __forceinline__ unsigned char *begin_tile(const Unit &u, int i, int c0, int c1,
+                                                     unsigned char *ring, int &nvalid) {
+  constexpr int kAhead = kStages - 2;
+  wait_tiles<D>(min(kAhead - 1, c1 - 1 - i));
+  lds_barrier();   // tile i visible to all waves; tile i-2's stage free
+  unsigned char *stage = ring + ((i - c0) % kStages) * Geo<D>::STAGE_BYTES;
+  nvalid = min(kTile, u.L - i * kTile);
+  if (nvalid < kTile) {
+    zero_value_tail<D>(stage, nvalid);
+    lds_barrier();
+  }
+  return stage;
 }
 
 // Context tiles [i0, ctx_end) of unit u through the LDS ring, in sub-ranges
 // whose pages fit the page-id cache.  LAG selects the wave-group role.
-template <int D, bool LAG>
+template <int D, bool BIG, bool LAG>
 __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, int i0, int ctx_end,
                                               unsigned char *ring, int *pcache,
-                                              const bf16x8 (&qr)[kQB][Geo<D>::KS], Acc<D> &A,
+                                              const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
                                               PTile<D> &P) {
   using G = Geo<D>;
   constexpr int kAhead = kStages - 2;  // tiles prefetched beyond the current one
@@ -534,30 +689,42 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
       pcache[k] = clamp_page(pt[pbase + k], p.num_pages);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
+    // the lag waves issue no loads when their lead partners carry them
+    constexpr bool kIssues = !LAG || kIssue == 1;
+    TilePages<D, BIG> pg;
+    if (kIssues) {
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j)
-      if (c0 + j < c1) issue_tile<D>(p, u, c0 + j, ring + (j % kStages) * G::STAGE_BYTES, pcache, pbase);
-    const unsigned char *prev = nullptr;
-    for (int i = c0; i < c1; ++i) {
-      wait_tiles<D>(min(kAhead - 1, c1 - 1 - i));
-      lds_barrier();   // tile i visible to all waves; tile i-2's stage free
-      unsigned char *stage = ring + ((i - c0) % kStages) * G::STAGE_BYTES;
-      if (i + kAhead < c1)
-        issue_tile<D>(p, u, i + kAhead, ring + ((i - c0 + kAhead) % kStages) * G::STAGE_BYTES,
-                      pcache, pbase);
-      const int nvalid = min(kTile, u.L - i * kTile);
-      if (nvalid < kTile) {
-        zero_value_tail<D>(stage, nvalid);
-        lds_barrier();
+      for (int j = 0; j < kAhead; ++j)
+        if (c0 + j < c1) {
+          read_pages<D, BIG>(p, u, c0 + j, pcache, pbase, pg);
+          issue_tile<D, BIG>(p, u, c0 + j, ring + (j % kStages) * G::STAGE_BYTES, pg);
+        }
+      if (c0 + kAhead < c1) read_pages<D, BIG>(p, u, c0 + kAhead, pcache, pbase, pg);
+    }
+    // Per tile i, the loads of tile i + kAhead are issued during its compute.
+    int nvalid;
+    auto loads = [&](int i) {
+      return TileLoads<D, BIG>{p, u, kIssues ? i + kAhead : c1,
+                               ring + ((i - c0 + kAhead) % kStages) * G::STAGE_BYTES, pg, pcache,
+                               pbase, c1};
+    };
+    if (!LAG) {
+      for (int i = c0; i < c1; ++i) {
+        const unsigned char *stage = begin_tile<D>(u, i, c0, c1, ring, nvalid);
+        tile_lead<D>(p, stage, nvalid, qr, A, P, loads(i));
       }
-      if (!LAG) {
-        tile_lead<D>(p, stage, nvalid, qr, A, P);
-      } else {
-        tile_lag<D>(p, prev, stage, nvalid, qr, A, P);
+    } else {
+      // the first tile has no predecessor; the last one's P.V drains after the loop
+      Batch buf[2];
+      const unsigned char *prev = begin_tile<D>(u, c0, c0, c1, ring, nvalid);
+      tile_lag<D, true>(p, nullptr, prev, nvalid, qr, A, P, buf, loads(c0));
+      for (int i = c0 + 1; i < c1; ++i) {
+        const unsigned char *stage = begin_tile<D>(u, i, c0, c1, ring, nvalid);
+        tile_lag<D, false>(p, prev, stage, nvalid, qr, A, P, buf, loads(i));
         prev = stage;
       }
+      pv_phase<D, false, false>(prev, nullptr, P, A, buf);
     }
-    if (LAG && prev) tile_pv<D>(prev, P, A);
     lds_barrier();   // ring and page cache free for reuse
   }
 }
@@ -572,103 +739,94 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
 // one wave's softmax (VALU) overlaps the other's MFMAs.  The lag group keeps
 // its probabilities for one tile; a tile's stage therefore stays live for two
 // iterations and only kStages - 2 tiles are prefetched.
-template <int D>
+template <int D, bool BIG>
 __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool complete,
                          int slot, unsigned char *ring, int *pcache) {
   using G = Geo<D>;
-  constexpr int kWaves = kThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int ln = lane & 31, hl = lane >> 5;
   const int M = p.S * p.g;
-  constexpr int WROWS = 32 * kQB;  // query rows per wave
   const bool lag = wave >= kWaves / 2;
 
-  // Q (B operand of S^T = K . Q^T): lane holds row ln of each 32-row block,
+  // Q (B operand of S^T = K . Q^T): lane holds query row 32*wave + ln,
   // features 16*ks + 8*hl .. +7.
-  bf16x8 qr[kQB][G::KS];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qi = u.qc * kQRows + wave * WROWS + qb * 32 + ln;
+  bf16x8 qr[G::KS];
+  {
+    const int qi = u.qc * kQRows + wave * 32 + ln;
     if (qi < M) {
       const int t = qi / p.g, j = qi % p.g;
       const __bf16 *src = p.q + (((size_t)u.b * p.S + t) * p.Hq + u.h * p.g + j) * D + 8 * hl;
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) qr[qb][ks] = *(const bf16x8 *)(src + 16 * ks);
+      for (int ks = 0; ks < G::KS; ++ks) qr[ks] = *(const bf16x8 *)(src + 16 * ks);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) qr[qb][ks] = bf16x8{};
+      for (int ks = 0; ks < G::KS; ++ks) qr[ks] = bf16x8{};
     }
   }
   Acc<D> A;
 #pragma unroll
-  for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) A.o[db][qb] = f32x16{};
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) { A.mref[qb] = -INFINITY; A.lsum[qb] = 0.f; }
+  for (int db = 0; db < G::DB; ++db) A.o[db] = f32x16{};
+  A.mref = -INFINITY;
+  A.lsum = 0.f;
   PTile<D> P;
 
   // ---- context tiles [i0, ctx_end): one loop instance per role, so that the
   // register allocation of each is independent (same barrier sequence)
   const int ctx_end = min(i1, u.nreal - 1);
-  if (lag) context_tiles<D, true>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
-  else context_tiles<D, false>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
+  if (lag) context_tiles<D, BIG, true>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
+  else context_tiles<D, BIG, false>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
   // ---- the block's own S keys/values (the unit's last real tile)
   if (i0 < u.nreal && i1 >= u.nreal) {
     unsigned char *stage = ring;
     stage_block_tile<D>(p, u, stage);
     lds_barrier();
-    tile_lead<D>(p, stage, p.S, qr, A, P);
+    tile_lead<D>(p, stage, p.S, qr, A, P, NoLoads{});
     lds_barrier();
   }
 
   // ---- epilogue.  O^T accumulator register r of lane (hl, ln) in block db
   // holds feature 32*db + 8*(r/4) + 4*hl + r%4 of query row ln.
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const float ltot = pair_sum(A.lsum[qb]);
-    const int qloc = wave * WROWS + qb * 32 + ln;
-    const int qi = u.qc * kQRows + qloc;
-    if (complete) {
-      if (qi < M) {
-        const float inv = 1.f / ltot;
-        const int t = qi / p.g, j = qi % p.g;
-        __bf16 *dst = p.out + (((size_t)u.b * p.S + t) * p.Hq + u.h * p.g + j) * D;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            f32x4 v = {A.o[db][qb][4 * r4 + 0] * inv, A.o[db][qb][4 * r4 + 1] * inv,
-                       A.o[db][qb][4 * r4 + 2] * inv, A.o[db][qb][4 * r4 + 3] * inv};
-            *(bf16x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = __builtin_convertvector(v, bf16x4);
-          }
-      }
-    } else {
-      // partial O^T / l in bf16, accumulator layout: 4 x bf16 (registers
-      // 4*r4 .. 4*r4+3) of lane l at ((((wave*kQB + qb)*DB + db)*4 + r4)*64 + l);
-      // features 32*db + 8*r4 + 4*(l/32) + 0..3 of query row
-      // wave*WROWS + qb*32 + l%32.  Normalising keeps the values in V's range.
-      const float inv = 1.f / ltot;
-      bf16x4 *wo = (bf16x4 *)(p.ws_o + (size_t)slot * D * kQRows);
+  const float ltot = pair_sum(A.lsum);
+  const float inv = 1.f / ltot;
+  const int qloc = wave * 32 + ln;
+  const int qi = u.qc * kQRows + qloc;
+  if (complete) {
+    if (qi < M) {
+      const int t = qi / p.g, j = qi % p.g;
+      __bf16 *dst = p.out + (((size_t)u.b * p.S + t) * p.Hq + u.h * p.g + j) * D;
 #pragma unroll
       for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 v = {A.o[db][qb][4 * r4] * inv, A.o[db][qb][4 * r4 + 1] * inv,
-                           A.o[db][qb][4 * r4 + 2] * inv, A.o[db][qb][4 * r4 + 3] * inv};
-          wo[(((wave * kQB + qb) * G::DB + db) * 4 + r4) * 64 + lane] = __builtin_convertvector(v, bf16x4);
+          const f32x4 v = {A.o[db][4 * r4 + 0] * inv, A.o[db][4 * r4 + 1] * inv,
+                           A.o[db][4 * r4 + 2] * inv, A.o[db][4 * r4 + 3] * inv};
+          *(bf16x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = __builtin_convertvector(v, bf16x4);
         }
-      if (hl == 0) {
-        float *wm = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
-        wm[0] = A.mref[qb];
-        wm[1] = ltot;
+    }
+  } else {
+    // partial O^T / l in bf16, accumulator layout: 4 x bf16 (registers
+    // 4*r4 .. 4*r4+3) of lane l at (((wave*DB + db)*4 + r4)*64 + l); features
+    // 32*db + 8*r4 + 4*(l/32) + 0..3 of query row 32*wave + l%32.
+    // Normalising keeps the values in V's range.
+    bf16x4 *wo = (bf16x4 *)(p.ws_o + (size_t)slot * D * kQRows);
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 v = {A.o[db][4 * r4] * inv, A.o[db][4 * r4 + 1] * inv,
+                         A.o[db][4 * r4 + 2] * inv, A.o[db][4 * r4 + 3] * inv};
+        wo[((wave * G::DB + db) * 4 + r4) * 64 + lane] = __builtin_convertvector(v, bf16x4);
       }
+    if (hl == 0) {
+      float *wm = p.ws_ml + ((size_t)slot * kQRows + qloc) * 2;
+      wm[0] = A.mref;
+      wm[1] = ltot;
     }
   }
 }
 
-template <int D>
+template <int D, bool BIG>
 __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char *ring = smem;
@@ -689,7 +847,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
     const int i1 = min(t_end, u.start + u.T) - u.start;
     // slot 0 holds the partial of the range's first unit, slot 1 its last
     if (i0 < u.nreal)
-      run_unit<D>(p, u, i0, i1, i0 == 0 && i1 >= u.nreal, 2 * blockIdx.x + (first ? 0 : 1), ring,
+      run_unit<D, BIG>(p, u, i0, i1, i0 == 0 && i1 >= u.nreal, 2 * blockIdx.x + (first ? 0 : 1), ring,
                   pcache);
     first = false;
     t = u.start + i1;
@@ -698,17 +856,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
 
 // Merges the partials of units cut by a range boundary:
 //   O = sum_w c_w (O_w / l_w) / sum_w c_w,  c_w = 2^(m_w - M) l_w,  M = max_w m_w.
-// One single-wave work-group per (unit, 16-feature slice, 64-row chunk);
-// thread = query row.  Contributors are the work-groups whose ranges meet
-// the unit's real tiles, w_lo .. w_hi; each left its partial in slot 2w, or
-// 2w + 1 for w_lo when its range began inside an earlier unit.  Four
-// contributors are read per step to keep enough loads in flight.
+// Work-group per (unit, 16-feature slice, 64-row chunk): lane = query row,
+// and the contributors (the work-groups whose ranges meet the unit's real
+// tiles, w_lo .. w_hi) are dealt round-robin to the waves, each keeping an
+// online (max, sum, O) over its share; the waves' states are then merged
+// through LDS.  Contributor w left its partial in slot 2w, or 2w + 1 for w_lo
+// when its range began inside an earlier unit.
 constexpr int kCombineRows = 64;
 constexpr int kCombineFeat = 16;
+constexpr int kCombineWaves = 4;
 constexpr int kCombineUnroll = 4;
 
 template <int D>
-__global__ __launch_bounds__(kCombineRows) void attn_combine_kernel(Params p) {
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(Params p) {
   const int upb = p.Hkv * p.qchunks;
   const int uid = blockIdx.x;
   const int b = uid / upb, ui = uid % upb;
@@ -721,27 +881,25 @@ __global__ __launch_bounds__(kCombineRows) void attn_combine_kernel(Params p) {
   const int R = (total + p.G - 1) / p.G;
   const int w_lo = us / R, w_hi = (us + nreal - 1) / R;
   if (w_lo == w_hi) return;  // finished in place by one work-group
-  const int qloc = blockIdx.z * kCombineRows + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qloc = blockIdx.z * kCombineRows + lane;
   const int qi = qc * kQRows + qloc;
-  if (qi >= p.S * p.g) return;
+  const bool row_ok = qi < p.S * p.g;
   const int lo_slot = 2 * w_lo + (w_lo * R != us ? 1 : 0);
   auto slot_of = [&](int w) { return w == w_lo ? lo_slot : 2 * w; };
-
-  float M = -INFINITY;
-  for (int w = w_lo; w <= w_hi; ++w) M = fmaxf(M, p.ws_ml[((size_t)slot_of(w) * kQRows + qloc) * 2]);
 
   // features f0 .. f0+15 of this row: 16-byte pieces at accumulator block
   // db = f0/32, register groups r4 = (f0%32)/8 + {0, 1}, lane halves hh = 0, 1
   const int f0 = kCombineFeat * blockIdx.y;
   const int db = f0 / 32, r40 = (f0 % 32) / 8;
-  constexpr int WROWS = 32 * kQB;
-  const int wv = qloc / WROWS, qb = (qloc % WROWS) / 32, ln = qloc % 32;
-  const size_t base = (((size_t)(wv * kQB + qb) * (D / 32) + db) * 4 + r40) * 64 + ln;
+  const int wv = qloc / 32, ln = qloc % 32;
+  const size_t base = (((size_t)wv * (D / 32) + db) * 4 + r40) * 64 + ln;
   float acc[kCombineFeat];
 #pragma unroll
   for (int e = 0; e < kCombineFeat; ++e) acc[e] = 0.f;
-  float lt = 0.f;
-  for (int w0 = w_lo; w0 <= w_hi; w0 += kCombineUnroll) {
+  float M = -INFINITY, lt = 0.f;
+  constexpr int kStep = kCombineWaves * kCombineUnroll;
+  for (int w0 = w_lo + wave * kCombineUnroll; row_ok && w0 <= w_hi; w0 += kStep) {
     f32x4 x[kCombineUnroll][4];
     float mw[kCombineUnroll], lw[kCombineUnroll];
 #pragma unroll
@@ -761,6 +919,13 @@ __global__ __launch_bounds__(kCombineRows) void attn_combine_kernel(Params p) {
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) {
       if (w0 + k > w_hi) break;
+      if (mw[k] > M) {  // new running max: rescale what this wave holds
+        const float f = __builtin_amdgcn_exp2f(M - mw[k]);
+        lt *= f;
+#pragma unroll
+        for (int e = 0; e < kCombineFeat; ++e) acc[e] *= f;
+        M = mw[k];
+      }
       const float wt = __builtin_amdgcn_exp2f(mw[k] - M) * lw[k];   // partials hold O / l
       lt += wt;
       // x[k][2*r + hh][e] is feature f0 + 8*r + 4*hh + e
@@ -772,36 +937,64 @@ __global__ __launch_bounds__(kCombineRows) void attn_combine_kernel(Params p) {
           for (int e = 0; e < 4; ++e) acc[8 * r + 4 * hh + e] += wt * x[k][2 * r + hh][e];
     }
   }
-  const float inv = 1.f / lt;
+  // merge the waves' (M, l, O) states
+  __shared__ float st[kCombineWaves][kCombineFeat + 2][kCombineRows];
+  st[wave][0][lane] = M;
+  st[wave][1][lane] = lt;
+#pragma unroll
+  for (int e = 0; e < kCombineFeat; ++e) st[wave][2 + e][lane] = acc[e];
+  __syncthreads();
+  if (wave != 0 || !row_ok) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < kCombineWaves; ++v) Mx = fmaxf(Mx, st[v][0][lane]);
+  float ltot = 0.f, o[kCombineFeat];
+#pragma unroll
+  for (int e = 0; e < kCombineFeat; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int v = 0; v < kCombineWaves; ++v) {
+    const float f = __builtin_amdgcn_exp2f(st[v][0][lane] - Mx);   // 0 for a wave without contributors
+    ltot += f * st[v][1][lane];
+#pragma unroll
+    for (int e = 0; e < kCombineFeat; ++e) o[e] += f * st[v][2 + e][lane];
+  }
+  const float inv = 1.f / ltot;
   const int t = qi / p.g, j = qi % p.g;
   __bf16 *dst = p.out + (((size_t)b * p.S + t) * p.Hq + h * p.g + j) * D + f0;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    f32x8 v = {acc[8 * c + 0] * inv, acc[8 * c + 1] * inv, acc[8 * c + 2] * inv, acc[8 * c + 3] * inv,
-               acc[8 * c + 4] * inv, acc[8 * c + 5] * inv, acc[8 * c + 6] * inv, acc[8 * c + 7] * inv};
+    f32x8 v = {o[8 * c + 0] * inv, o[8 * c + 1] * inv, o[8 * c + 2] * inv, o[8 * c + 3] * inv,
+               o[8 * c + 4] * inv, o[8 * c + 5] * inv, o[8 * c + 6] * inv, o[8 * c + 7] * inv};
     *(bf16x8 *)(dst + 8 * c) = __builtin_convertvector(v, bf16x8);
   }
 }
 
-template <int D>
-hipError_t launch_d(const Params &prm, hipStream_t stream) {
+template <int D, bool BIG>
+hipError_t launch_split(const Params &prm, hipStream_t stream) {
   const size_t pre_bytes = (size_t)(2 * prm.B + 1) * sizeof(int);   // pre[] and lens[]
   const size_t split_lds = Geo<D>::RING_BYTES + kPageCache * sizeof(int) + pre_bytes;
   static bool attr_done = false;   // benign race: every caller sets the same value
   if (!attr_done) {
-    const hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<D>,
+    const hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<D, BIG>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)(Geo<D>::RING_BYTES + kPageCache * sizeof(int) +
                                                    (2 * kMaxBatch + 1) * sizeof(int)));
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(attn_split_kernel<D>, dim3(prm.G), dim3(kThreads), split_lds, stream, prm);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((attn_split_kernel<D, BIG>), dim3(prm.G), dim3(kThreads), split_lds, stream, prm);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const Params &prm, hipStream_t stream) {
+  // pages of at least one tile: every tile lies inside one page
+  hipError_t e = prm.page_size >= kTile ? launch_split<D, true>(prm, stream)
+                                        : launch_split<D, false>(prm, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel<D>,
                      dim3(prm.B * prm.Hkv * prm.qchunks, D / kCombineFeat, kQRows / kCombineRows),
-                     dim3(kCombineRows), 0, stream, prm);
+                     dim3(64 * kCombineWaves), 0, stream, prm);
   return hipGetLastError();
 }
 
