@@ -90,7 +90,7 @@ def _read_counters(path, counter):
     return per
 
 
-def summarize_pmc(fetch_csv, write_csv, out_md):
+def summarize_pmc(fetch_csv, write_csv, out_md, command=""):
     fetch = _read_counters(fetch_csv, "FETCH_SIZE")
     write = _read_counters(write_csv, "WRITE_SIZE")
     # the calibration copy is the largest copy dispatch
@@ -113,23 +113,30 @@ def summarize_pmc(fetch_csv, write_csv, out_md):
         lines.append("| %s | %d | %.0f | %.0f | %.3e |" % (k, len(fetch.get(k, [])), f, w, b))
         rec[k] = {"fetch_kib": f, "write_kib": w, "bytes": b}
     rec["hbm_bytes_per_launch"] = total
-    lines += ["", "HBM bytes per tt_block_attn launch (split + combine): %.4e" % total, "",
-              "COUNTERS_JSON " + json.dumps(rec)]
+    lines += ["", "HBM bytes per tt_block_attn launch (split + combine): %.4e" % total, ""]
+    if command:
+        lines += ["Command (run from /tmp on the GPU host, REPO = the repository root):", "", "```",
+                  command, "```", ""]
+    lines += ["COUNTERS_JSON " + json.dumps(rec)]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def summarize_stats(stats_csv, out_md):
+def summarize_stats(stats_csv, out_md, command=""):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
     lines = ["# Kernel time summary (rocprofv3 --kernel-trace --stats)", "",
-             "| kernel | calls | avg us | total % |", "|---|---|---|---|"]
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
     for r in rows[:12]:
-        name = r["Name"]
-        short = name.split("(")[0].replace("void ", "").replace("tt::(anonymous namespace)::", "")
-        lines.append("| %s | %s | %.2f | %.2f |" % (short[:80], r["Calls"], float(r["AverageNs"]) / 1e3,
-                                                   float(r["Percentage"])))
+        name = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+        short = name.split("(")[0]
+        lines.append("| %s | %s | %.2f | %.2f | %.2f | %.2f |" % (
+            short[:80], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    if command:
+        lines += ["", "Command (run from /tmp on the GPU host, REPO = the repository root):", "", "```",
+                  command, "```"]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -149,12 +156,14 @@ def main():
                     help="turn two rocprofv3 --pmc counter_collection.csv files into a summary")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a summary")
+    ap.add_argument("--profile-command", default="",
+                    help="command line recorded in a --summarize-* summary")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc)
+        summarize_pmc(*args.summarize_pmc, command=args.profile_command)
         return
     if args.summarize_stats:
-        summarize_stats(*args.summarize_stats)
+        summarize_stats(*args.summarize_stats, command=args.profile_command)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -195,16 +195,20 @@ __device__ __forceinline__ void lds_barrier() {
 // vmcnt-only s_waitcnt immediate (gfx9 encoding; expcnt/lgkmcnt left at max).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-// Which waves issue the direct loads.  kIssue = 1: every wave issues its own
-// share of a tile; 2: each lead wave w also issues the share of its lag
-// partner w + waves/2, so that the lag waves, which carry the longer compute,
-// never block on a full memory queue.
-#ifndef TT_ATTN_ISSUE
-#define TT_ATTN_ISSUE 2
+// Which waves issue the direct loads.  kIssuer 0: every wave issues its own
+// share of a tile when its compute starts; 1: each lead wave w issues its
+// share and that of its lag partner w + waves/2 when its compute starts;
+// 2: each lag wave issues both shares when its compute ends, where it would
+// otherwise wait at the barrier for the lead wave; 3: every wave issues its
+// own share, lead waves when their compute starts, lag waves when it ends.
+#ifndef TT_ATTN_ISSUER
+#define TT_ATTN_ISSUER 1
 #endif
+constexpr int kIssuer = TT_ATTN_ISSUER;
+#define TT_ATTN_ISSUE ((kIssuer == 0 || kIssuer == 3) ? 1 : 2)
 constexpr int kIssue = TT_ATTN_ISSUE;
 constexpr int kWaves = kThreads / 64;
-static_assert(kIssue == 1 || kIssue == 2, "shares per issuing wave");
+static_assert(kIssuer >= 0 && kIssuer <= 3, "issuer mode");
 
 // Wait until at most `tiles_after` tiles' worth of this wave's direct loads
 // are in flight.
@@ -248,6 +252,10 @@ __device__ __forceinline__ void value_slot(int iw, int n, int &d, int &c) {
   c = (slot & 7) ^ ((d & 7) ^ ((d >> 3) & 1));
 }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// Index of this wave among the issuing waves.
+__device__ __forceinline__ int issuer_id() {
+  return kIssuer == 2 ? wave_id() - kWaves / 2 : wave_id();
+}
 // Positions past the context are clamped to a valid token: keys there are
 // masked by score, values are zeroed in LDS before use.
 __device__ __forceinline__ int key_pos(const Unit &u, int i, int t) {
@@ -276,7 +284,7 @@ __device__ __forceinline__ void read_pages(const Params &p, const Unit &u, int i
   if constexpr (BIG) {
     pg.pg = pcache[((i * kTile) >> p.lps) - pbase];
   } else {
-    const int iw = wave_id();
+    const int iw = issuer_id();
 #pragma unroll
     for (int n = 0; n < Share<D>::NK; ++n) {
       int t, c;
@@ -313,7 +321,7 @@ template <int D, bool BIG>
 __device__ __forceinline__ void issue_tile(const Params &p, const Unit &u, int i,
                                            unsigned char *stage, const TilePages<D, BIG> &pg) {
   using G = Geo<D>;
-  const int iw = wave_id();
+  const int iw = issuer_id();
   const int pmask = p.page_size - 1;
   unsigned char *kl = stage + iw * Share<D>::NK * 1024;
   unsigned char *vl = stage + G::K_BYTES + iw * Share<D>::NV * 1024;
@@ -643,7 +651,7 @@ __device__ __forceinline__ void tile_lag(const Params &p, const unsigned char *p
                                          const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
                                          PTile<D> &P, Batch (&buf)[2], const Loads &ld) {
   f32x16 s[2];
-  ld.issue();
+  if (kIssuer < 2) ld.issue();
   if (FIRST) {
     read_qk<D>(stage, 0, buf[0]);
   } else {
@@ -651,6 +659,10 @@ __device__ __forceinline__ void tile_lag(const Params &p, const unsigned char *p
   }
   score_phase<D, true>(stage, qr, s, buf);
   softmax_tile<D>(p, s, nvalid, A, P);
+  if (kIssuer >= 2) {
+    sched_fence();
+    ld.issue();
+  }
 }
 
 // Start of context tile i of a sub-range [c0, c1): waits for the tile and
@@ -690,7 +702,7 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     // the lag waves issue no loads when their lead partners carry them
-    constexpr bool kIssues = !LAG || kIssue == 1;
+    constexpr bool kIssues = kIssuer == 0 || kIssuer == 3 || (kIssuer == 1) == !LAG;
     TilePages<D, BIG> pg;
     if (kIssues) {
 #pragma unroll
