@@ -63,6 +63,8 @@ def _load():
         lib.tto_block_attn.restype = I
         lib.tto_unmask.argtypes = [I, I, I, P, P, P, I, P, P, P]
         lib.tto_unmask.restype = I
+        lib.tto_unmask_threshold.argtypes = [I, I, I, P, P, ctypes.c_double, P, P, P, P]
+        lib.tto_unmask_threshold.restype = I
         lib.tto_num_threads.argtypes = []
         lib.tto_num_threads.restype = I
         _lib = lib
@@ -156,6 +158,55 @@ def unmask(logits: np.ndarray, mask: np.ndarray, k_commit: Optional[np.ndarray] 
     if err:
         raise ValueError("oracle unmask failed with code %d" % err)
     return ids, commit, conf
+
+
+def unmask_threshold(logits: np.ndarray, mask: np.ndarray, gamma: float,
+                     nsteps: Optional[np.ndarray] = None):
+    """Threshold form of the commit rule: every masked position with confidence
+    strictly above ``gamma`` is committed; when none is, the most confident
+    masked position is (lower position on ties).  Returns (ids int32 [B,S],
+    commit uint8 [B,S], conf float64 [B,S], nsteps int32 [B]) where nsteps is
+    the input count (zeros if None) plus one for each sequence that had a
+    masked position."""
+    mask = _c(mask, np.uint8)
+    B, S = mask.shape
+    logits = _c(logits, np.float32).reshape(B * S, -1)
+    V = logits.shape[1]
+    ids = np.zeros((B, S), dtype=np.int32)
+    commit = np.zeros((B, S), dtype=np.uint8)
+    conf = np.zeros((B, S), dtype=np.float64)
+    ns = np.zeros(B, np.int32) if nsteps is None else np.array(nsteps, dtype=np.int32, copy=True)
+    err = _load().tto_unmask_threshold(B, S, V, _ptr(logits), _ptr(mask), float(gamma), _ptr(ids),
+                                       _ptr(commit), _ptr(conf), _ptr(ns))
+    if err:
+        raise ValueError("oracle threshold unmask failed with code %d" % err)
+    return ids, commit, conf, ns
+
+
+def adaptive_unmask_loop(logits_per_step: Sequence[np.ndarray], B: int, S: int, gamma: float,
+                         max_steps: int):
+    """The adaptive-step sampler of one block ("Training and sampling",
+    paperfeed review): starting from an all-masked block, each step commits by
+    the threshold rule and clears the committed mask bits, until every
+    sequence's block is resolved or ``max_steps`` steps have run (the pages'
+    budget is 16).  Step s uses logits_per_step[s % len(logits_per_step)].
+
+    Returns a dict with per-step ``ids``, ``commit``, ``conf``, ``mask`` (after
+    the step), the final ``nsteps`` per sequence and ``steps`` run."""
+    mask = np.ones((B, S), dtype=np.uint8)
+    ns = np.zeros(B, np.int32)
+    res = {"ids": [], "commit": [], "conf": [], "mask": []}
+    s = 0
+    while s < max_steps and mask.any():
+        lg = logits_per_step[s % len(logits_per_step)]
+        ids, commit, conf, ns = unmask_threshold(lg, mask, gamma, ns)
+        mask = (mask & (1 - commit)).astype(np.uint8)
+        res["ids"].append(ids); res["commit"].append(commit); res["conf"].append(conf)
+        res["mask"].append(mask.copy())
+        s += 1
+    res["nsteps"] = ns
+    res["steps"] = s
+    return res
 
 
 def kv_append(k_pages: np.ndarray, v_pages: np.ndarray, page_table: np.ndarray,

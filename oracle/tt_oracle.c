@@ -229,6 +229,51 @@ int tto_unmask(int B, int S, int V, const float *logits, const uint8_t *mask,
   return TTO_OK;
 }
 
+/*
+ * Threshold form of the commit rule.
+ *
+ * [REVIEW, "Training and sampling"]: at each step every masked position is
+ * predicted and each prediction whose confidence is above gamma (0.8 on the
+ * pages) is committed; the number committed per step adapts to the text.
+ * [SKY, "Generating Text in Parallel Like Solving a Sudoku"]: commit the
+ * positions whose confidence exceeds the threshold, re-mask the rest, run
+ * again.  Readings: "above"/"exceeds" is strict (conf > gamma).  The pages
+ * do not say what a step does when no masked position clears gamma; here it
+ * commits the single most confident masked position (ties to the lower
+ * position), so every step makes progress.  Committed positions are never
+ * candidates.
+ *
+ * ids/conf are written for every row (as in tto_unmask); commit[b*S+t] = 1
+ * exactly on the committed positions.  nsteps (may be NULL) counts, per
+ * sequence, the calls that found at least one masked position.
+ */
+int tto_unmask_threshold(int B, int S, int V, const float *logits, const uint8_t *mask,
+                         double gamma, int32_t *ids, uint8_t *commit, double *conf,
+                         int32_t *nsteps) {
+  if (B < 0 || S < 1 || V < 1) return TTO_ERR_ARG;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < B * S; ++r) row_conf(logits + (size_t)r * V, V, ids + r, conf + r);
+
+  for (int b = 0; b < B; ++b) {
+    int n = 0, n_above = 0, best = -1;
+    for (int t = 0; t < S; ++t) {
+      const size_t r = (size_t)b * S + t;
+      commit[r] = 0;
+      if (!mask[r]) continue;
+      ++n;
+      if (conf[r] > gamma) {
+        commit[r] = 1;
+        ++n_above;
+      }
+      /* most confident masked position; strict > keeps the lower one on ties */
+      if (best < 0 || conf[r] > conf[(size_t)b * S + best]) best = t;
+    }
+    if (n > 0 && n_above == 0) commit[(size_t)b * S + best] = 1;
+    if (nsteps && n > 0) nsteps[b] += 1;
+  }
+  return TTO_OK;
+}
+
 /* Threads the OpenMP runtime will use (for reporting). */
 int tto_num_threads(void) {
 #ifdef _OPENMP

@@ -33,6 +33,12 @@ MUTATIONS = [
      "if (cj > cx || (cj == cx && cand[j] > x)) break;"),
     ("commit_unmasked_too", "if (mask[(size_t)b * S + t]) cand[n++] = t;", "cand[n++] = t;"),
     ("remaining_floor", "((long)n + remaining_steps - 1) / remaining_steps", "(long)n / remaining_steps"),
+    ("threshold_not_strict", "if (conf[r] > gamma) {", "if (conf[r] >= gamma) {"),
+    ("threshold_no_fallback", "if (n > 0 && n_above == 0) commit[(size_t)b * S + best] = 1;", ""),
+    ("fallback_higher_slot_on_tie", "if (best < 0 || conf[r] > conf[(size_t)b * S + best]) best = t;",
+     "if (best < 0 || conf[r] >= conf[(size_t)b * S + best]) best = t;"),
+    ("threshold_ignores_mask", "      if (!mask[r]) continue;\n      ++n;", "      ++n;"),
+    ("nsteps_counts_empty", "if (nsteps && n > 0) nsteps[b] += 1;", "if (nsteps) nsteps[b] += 1;"),
 ]
 
 
@@ -77,8 +83,23 @@ def _pins_pass():
             _, commit, conf = oracle.unmask(lg, m, np.array([k], np.int32))
             if not np.array_equal(commit[0], _brute_force(conf[0], m[0], k)):
                 return False
+        if not _threshold_pins_pass():
+            return False
     except ValueError:
         return False
+    return True
+
+
+def _threshold_pins_pass():
+    import test_oracle_threshold as T
+    checks = [T.test_hand_sequence_by_gamma, T.test_hand_fallback_tie, T.test_hand_empty_mask,
+              T.test_hand_adaptive_loop, T.test_loop_budget_stops_unresolved_blocks]
+    checks += [lambda: T.test_gamma_one_is_top1(0), lambda: T.test_negative_gamma_commits_every_masked(0)]
+    for f in checks:
+        try:
+            f()
+        except AssertionError:
+            return False
     return True
 
 
