@@ -178,6 +178,32 @@ int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit,
               int32_t *ids_out, uint8_t *commit_out, float *conf_out, uint32_t flags,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Threshold form of the commit rule, the one the pages' sampler uses
+ * ("Training and sampling", paperfeed review: every prediction whose
+ * confidence is above gamma = 0.8 is committed and the count per step
+ * adapts; "Generating Text in Parallel Like Solving a Sudoku", kongchang
+ * explainer: commit the positions whose confidence exceeds the threshold,
+ * re-mask the rest).  ids_out and conf are as in tt_unmask.  Per sequence b,
+ * every masked slot with conf > gamma is committed; when no masked slot
+ * clears gamma, the single most confident masked slot is (lower slot on
+ * equal conf), so every step makes progress.  A sequence with nothing masked
+ * commits nothing.  Driving this call until every mask is clear is the
+ * adaptive-step loop: sequences resolve their block at different steps.
+ *
+ *   logits, mask, batch, block, vocab, ids_out, commit_out, conf_out, flags,
+ *   workspace   as in tt_unmask (same workspace size)
+ *   gamma       confidence threshold (finite)
+ *   nsteps      int32 [B] or NULL: incremented for every sequence that had at
+ *               least one masked slot on entry (steps used so far)
+ *
+ * The comparison conf > gamma is taken on the fp32 confidence.
+ */
+int tt_unmask_threshold(const float *logits, uint8_t *mask, float gamma, int32_t batch,
+                        int32_t block, int32_t vocab, int32_t *ids_out, uint8_t *commit_out,
+                        float *conf_out, int32_t *nsteps, uint32_t flags, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *tt_status_str(int status);
 

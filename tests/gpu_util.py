@@ -109,3 +109,35 @@ def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff):
             cstar = masked_conf[k_eff[b] - 1]
             assert np.all(np.abs(conf_ref[b][diff] - cstar) <= COMMIT_TIE), \
                 (b, diff, conf_ref[b][diff], cstar)
+
+
+def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma):
+    """Threshold-rule comparator.  The GPU decides conf > gamma on its fp32
+    confidence, the oracle's confidence is fp64, so a slot whose oracle
+    confidence lies within COMMIT_TIE of gamma may go either way; the same band
+    applies to ties of the fallback's maximum.  Everything else is fixed:
+    only masked slots commit; slots surely above gamma commit, slots surely
+    below it do not (unless a fallback); a fallback commits exactly one slot
+    among the most confident."""
+    B, S = mask.shape
+    for b in range(B):
+        cg = commit_gpu[b].astype(bool)
+        m = mask[b].astype(bool)
+        c = conf_ref[b]
+        assert not np.any(cg & ~m), "committed an unmasked slot in sequence %d" % b
+        if not m.any():
+            assert not cg.any()
+            continue
+        sure = m & (c > gamma + COMMIT_TIE)
+        near = m & (np.abs(c - gamma) <= COMMIT_TIE)
+        if sure.any():
+            assert np.all(cg[sure]), (b, "a slot surely above gamma was not committed")
+            assert not np.any(cg & m & ~sure & ~near), (b, "a slot surely below gamma committed")
+            continue
+        # nothing surely above: either the GPU judged some near-gamma slots
+        # above gamma (then exactly those commit), or none (then the fallback
+        # commits one slot whose confidence is within the band of the maximum)
+        assert cg.any(), (b, "no progress")
+        judged_above = np.all(near[cg])
+        fallback = cg.sum() == 1 and abs(c[cg][0] - c[m].max()) <= COMMIT_TIE
+        assert judged_above or fallback, (b, np.nonzero(cg)[0], c[cg], c[m].max())

@@ -161,3 +161,32 @@ def test_unmask_nulls(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(tt.LibraryMissing):
         tt.load_library(str(tmp_path / "nope.so"))
+
+
+THRESH_BAD = [
+    ("block0", dict(S=0), -2),
+    ("vocab0", dict(V=0), -2),
+    ("gamma_nan", dict(gamma=float("nan")), -2),
+    ("gamma_inf", dict(gamma=float("inf")), -2),
+    ("flags", dict(flags=2), -4),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", THRESH_BAD, ids=[u[0] for u in THRESH_BAD])
+def test_unmask_threshold_validation(lib, name, kw, code):
+    a = dict(B=2, S=16, V=1024, gamma=0.8, flags=0)
+    a.update(kw)
+    st = lib.tt_unmask_threshold(FAKE, FAKE, a["gamma"], a["B"], a["S"], a["V"], FAKE, FAKE, None,
+                                 None, a["flags"], FAKE, ctypes.c_size_t(1 << 30), None)
+    assert st == code
+
+
+def test_unmask_threshold_nulls_and_workspace(lib):
+    st = lib.tt_unmask_threshold(FAKE, None, 0.8, 2, 16, 1024, FAKE, FAKE, None, None, 0, FAKE,
+                                 ctypes.c_size_t(1 << 30), None)
+    assert st == -1
+    st = lib.tt_unmask_threshold(FAKE, FAKE, 0.8, 2, 16, 131072, FAKE, FAKE, None, None, 0, FAKE,
+                                 ctypes.c_size_t(16), None)
+    assert st == tt.load_library().tt_unmask(FAKE, FAKE, None, 1, 2, 16, 131072, FAKE, FAKE, None,
+                                             0, FAKE, ctypes.c_size_t(16), None)
+    assert st == -5

@@ -24,8 +24,8 @@ TT_F32 = 1
 TT_UNMASK_UPDATE_MASK = 1
 
 EXPORTS = ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_kv_append",
-           "tt_unmask_workspace_bytes", "tt_unmask", "tt_status_str", "tt_last_error",
-           "tt_abi_version")
+           "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold", "tt_status_str",
+           "tt_last_error", "tt_abi_version")
 
 
 class LibraryMissing(ImportError):
@@ -66,6 +66,8 @@ def load_library(path: Optional[str] = None):
     lib.tt_kv_append.argtypes = [DP, P, P, P, P, P, P, P]
     lib.tt_unmask_workspace_bytes.argtypes = [I32, I32, I32, ctypes.POINTER(SZ)]
     lib.tt_unmask.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, ctypes.c_uint32, P, SZ, P]
+    lib.tt_unmask_threshold.argtypes = [P, P, ctypes.c_float, I32, I32, I32, P, P, P, P,
+                                        ctypes.c_uint32, P, SZ, P]
     lib.tt_status_str.argtypes = [ctypes.c_int]
     lib.tt_status_str.restype = ctypes.c_char_p
     lib.tt_last_error.argtypes = []
@@ -193,4 +195,20 @@ def tt_unmask(logits, mask, k_commit, remaining_steps: int, ids_out, commit_out,
         B, S, V, _ptr(ids_out, "ids_out", torch.int32, B * S),
         _ptr(commit_out, "commit_out", torch.uint8, B * S),
         _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True), int(flags),
+        _ptr(workspace, "workspace", allow_none=True), nbytes, _stream(stream)))
+
+
+def tt_unmask_threshold(logits, mask, gamma: float, ids_out, commit_out, conf_out=None,
+                        nsteps=None, flags: int = 0, workspace=None, stream=None) -> None:
+    """Threshold form of the commit rule (see include/tt.h)."""
+    torch = _torch()
+    B, S = mask.shape
+    V = logits.shape[-1]
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().tt_unmask_threshold(
+        _ptr(logits, "logits", torch.float32, B * S * V), _ptr(mask, "mask", torch.uint8, B * S),
+        float(gamma), B, S, V, _ptr(ids_out, "ids_out", torch.int32, B * S),
+        _ptr(commit_out, "commit_out", torch.uint8, B * S),
+        _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True),
+        _ptr(nsteps, "nsteps", torch.int32, B, allow_none=True), int(flags),
         _ptr(workspace, "workspace", allow_none=True), nbytes, _stream(stream)))

@@ -8,6 +8,8 @@
 #include <atomic>
 #include <string>
 
+#include <cmath>
+
 #include "tt_internal.h"
 
 namespace {
@@ -221,6 +223,33 @@ int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit, int32
   const hipError_t e = tt::launch_unmask(plan, logits, mask, k_commit, remaining_steps, ids_out,
                                          commit_out, conf_out, flags, workspace,
                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int tt_unmask_threshold(const float *logits, uint8_t *mask, float gamma, int32_t B, int32_t S,
+                        int32_t V, int32_t *ids_out, uint8_t *commit_out, float *conf_out,
+                        int32_t *nsteps, uint32_t flags, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  int st = check_unmask_shape(B, S, V);
+  if (st) return st;
+  if (flags & ~TT_UNMASK_UPDATE_MASK) return fail(TT_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (!std::isfinite(gamma)) return fail(TT_ERR_SHAPE, "gamma must be finite");
+  if (B == 0) return ok();
+  if (!logits || !mask || !ids_out || !commit_out)
+    return fail(TT_ERR_NULL, "logits, mask, ids_out and commit_out are required");
+  if (!aligned(logits, 4) || !aligned(ids_out, 4) || (nsteps && !aligned(nsteps, 4)) ||
+      (conf_out && !aligned(conf_out, 4)))
+    return fail(TT_ERR_UNSUPPORTED, "logits, ids_out, nsteps, conf_out must be 4-byte aligned");
+  const tt::UnmaskPlan plan = tt::plan_unmask(B, S, V);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(TT_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (device_cus(nullptr) <= 0) return fail(TT_ERR_NO_DEVICE, "no HIP device");
+  const hipError_t e = tt::launch_unmask_threshold(plan, logits, mask, gamma, ids_out, commit_out,
+                                                   conf_out, nsteps, flags, workspace,
+                                                   (hipStream_t)stream);
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -59,4 +59,9 @@ hipError_t launch_unmask(const UnmaskPlan &p, const float *logits, uint8_t *mask
                          uint8_t *commit, float *conf, uint32_t flags, void *workspace,
                          hipStream_t stream);
 
+hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uint8_t *mask,
+                                   float gamma, int32_t *ids, uint8_t *commit, float *conf,
+                                   int32_t *nsteps, uint32_t flags, void *workspace,
+                                   hipStream_t stream);
+
 }  // namespace tt

@@ -2,7 +2,9 @@
 // Text in Parallel Like Solving a Sudoku", kongchang explainer): for every
 // row of logits the greedy id (lowest index among equal maxima) and its
 // softmax probability 1/Z, Z = sum_v exp(l_v - max); then per sequence the
-// k most confident masked slots are committed (equal confidence: lower slot).
+// k most confident masked slots are committed (equal confidence: lower slot),
+// or, in the threshold form, every masked slot above gamma (the most
+// confident one when none is).
 //
 // Kernel 1 (rowreduce) streams the fp32 logits once, HBM-bound: each work-
 // group reduces one vocabulary chunk of one row to (max, lowest argmax,
@@ -156,6 +158,55 @@ __global__ __launch_bounds__(64) void unmask_commit_kernel(const Part *parts, in
   }
 }
 
+// Threshold form: every masked slot with conf > gamma commits; if none does,
+// the masked slot ranked first by (conf desc, slot asc) does.  One wave per
+// sequence, as the count form.
+__global__ __launch_bounds__(64) void unmask_threshold_commit_kernel(
+    const Part *parts, int chunks, int S, uint8_t *mask, float gamma, int32_t *ids,
+    uint8_t *commit, float *conf, int32_t *nsteps, uint32_t flags) {
+  __shared__ float cs[64];
+  __shared__ int ms[64];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const size_t r = (size_t)b * S + t;
+  float c = 0.f;
+  int id = 0, mk = 0;
+  if (t < S) {
+    Acc a;
+    a.init();
+    for (int k = 0; k < chunks; ++k) {
+      const Part pt = parts[r * chunks + k];
+      a.merge(pt.m, pt.s, pt.idx);
+    }
+    c = 1.f / a.s;
+    id = a.idx == INT_MAX ? 0 : a.idx;
+    mk = mask[r] != 0;
+  }
+  cs[t] = c;
+  ms[t] = mk;
+  __syncthreads();
+  int n = 0, n_above = 0;
+  for (int u = 0; u < S; ++u) {
+    n += ms[u];
+    n_above += (ms[u] && cs[u] > gamma) ? 1 : 0;
+  }
+  if (t < S) {
+    int com;
+    if (n_above > 0) {
+      com = (mk && c > gamma) ? 1 : 0;
+    } else {
+      int rank = 0;
+      for (int u = 0; u < S; ++u)
+        rank += (ms[u] && (cs[u] > c || (cs[u] == c && u < t))) ? 1 : 0;
+      com = (mk && rank == 0) ? 1 : 0;
+    }
+    ids[r] = id;
+    commit[r] = (uint8_t)com;
+    if (conf) conf[r] = c;
+    if ((flags & TT_UNMASK_UPDATE_MASK) && com) mask[r] = 0;
+  }
+  if (t == 0 && nsteps && n > 0) nsteps[b] += 1;
+}
+
 }  // namespace
 
 UnmaskPlan plan_unmask(int B, int S, int V) {
@@ -175,18 +226,35 @@ UnmaskPlan plan_unmask(int B, int S, int V) {
   return p;
 }
 
+static hipError_t launch_rowreduce(const UnmaskPlan &p, const float *logits, Part *parts,
+                                   hipStream_t stream) {
+  const int vec = (p.V % 4 == 0) && (((uintptr_t)logits & 15) == 0);
+  hipLaunchKernelGGL(unmask_rowreduce_kernel, dim3(p.chunks, p.B * p.S), dim3(kThreads), 0,
+                     stream, logits, p.V, p.chunk_len, p.chunks, vec, parts);
+  return hipGetLastError();
+}
+
 hipError_t launch_unmask(const UnmaskPlan &p, const float *logits, uint8_t *mask,
                          const int32_t *k_commit, int remaining_steps, int32_t *ids,
                          uint8_t *commit, float *conf, uint32_t flags, void *workspace,
                          hipStream_t stream) {
   Part *parts = (Part *)workspace;
-  const int vec = (p.V % 4 == 0) && (((uintptr_t)logits & 15) == 0);
-  hipLaunchKernelGGL(unmask_rowreduce_kernel, dim3(p.chunks, p.B * p.S), dim3(kThreads), 0,
-                     stream, logits, p.V, p.chunk_len, p.chunks, vec, parts);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_rowreduce(p, logits, parts, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(unmask_commit_kernel, dim3(p.B), dim3(64), 0, stream, parts, p.chunks, p.S,
                      mask, k_commit, remaining_steps, ids, commit, conf, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uint8_t *mask,
+                                   float gamma, int32_t *ids, uint8_t *commit, float *conf,
+                                   int32_t *nsteps, uint32_t flags, void *workspace,
+                                   hipStream_t stream) {
+  Part *parts = (Part *)workspace;
+  hipError_t e = launch_rowreduce(p, logits, parts, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(unmask_threshold_commit_kernel, dim3(p.B), dim3(64), 0, stream, parts,
+                     p.chunks, p.S, mask, gamma, ids, commit, conf, nsteps, flags);
   return hipGetLastError();
 }
 

@@ -228,3 +228,43 @@ def config5(seed: int = 5, B: int = 32, layers: int = 6, steps: int = 4,
     return Loop(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, layers=layers, steps=steps,
                 vocab=vocab, page_size=page_size, pools=pools, q=q, k_blk=kb,
                 v_blk=vb, logits=logits, seed=seed)
+
+
+# ---------------------------------------------------------------------------
+# Peaked logits for the threshold (adaptive-step) sampler.  N(0, 3^2) logits
+# over a large vocabulary never give a greedy probability near 0.8, so each
+# row gets one spiked entry whose height sets its confidence.  The shape of
+# the schedule follows what the pages report about the sampler: most slots
+# resolve at the first step, the rest over a short tail, earlier slots more
+# readily than later ones.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PeakedBlock:
+    B: int
+    S: int
+    vocab: int
+    difficulty: np.ndarray      # [B*S] in [0, 1)
+    spike_ids: np.ndarray       # [B*S] int64, the entry that is spiked in every step
+    seed: int
+
+
+def make_peaked_block(rng: np.random.Generator, B: int, S: int, vocab: int,
+                      seed: int = 0) -> PeakedBlock:
+    return PeakedBlock(B=B, S=S, vocab=vocab, difficulty=rng.random(B * S),
+                       spike_ids=rng.integers(0, vocab, size=B * S), seed=seed)
+
+
+def peaked_logits(rng: np.random.Generator, blk: PeakedBlock, step: int,
+                  sigma: float = 3.0) -> np.ndarray:
+    """fp32 logits [B*S, vocab] for one sampler step: N(0, sigma^2) plus, per
+    row, a spike of height ln(vocab) + sigma^2/2 + margin at spike_ids, where
+    margin = 4 - 4*difficulty - 0.15*slot + step + 0.3*N(0, 1).  A margin of
+    about ln 4 puts the greedy probability near 0.8."""
+    rows = blk.B * blk.S
+    x = _draw(rng, (rows, blk.vocab), "f32", sigma)
+    slot = np.tile(np.arange(blk.S), blk.B)
+    margin = 4.0 - 4.0 * blk.difficulty - 0.15 * slot + step + 0.3 * rng.standard_normal(rows)
+    height = np.log(blk.vocab) + 0.5 * sigma * sigma + margin
+    x[np.arange(rows), blk.spike_ids] = height.astype(np.float32)
+    return x
