@@ -42,10 +42,10 @@ def log(msg):
 
 
 def attn_source_hash():
+    """Identifies the attention kernel source the counters were taken on."""
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "tt_internal.h"):
-        with open(os.path.join(ROOT, "two_tower_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    with open(os.path.join(ROOT, "two_tower_attention_amd", "csrc", "attn_bf16.hip"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -287,18 +287,50 @@ def main():
     attn_tfs = attn_flops / attn_s / 1e12
     log("attention: %.1f us/launch, %.0f GB/s, %.0f TFLOP/s" % (attn_s * 1e6, attn_gbs, attn_tfs))
 
-    # ---- unmask alone
+    # ---- unmask alone (flags 0: the all-masked state is left untouched)
+    mask.copy_(ones)
     u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_un = 16
     u0.record(stream)
     for it in range(n_un):
-        mask.copy_(ones)
         tt.tt_unmask(logits[it % T], mask, None, 4, ids, com, None, 0, uws)
     u1.record(stream)
     torch.cuda.synchronize()
     un_s = u0.elapsed_time(u1) / 1e3 / n_un
     un_gbs = B * S * V * 4 / un_s / 1e9
     log("unmask: %.1f us/call, %.0f GB/s" % (un_s * 1e6, un_gbs))
+
+    # ---- threshold form of the commit rule (gamma = 0.8) on peaked logits:
+    # the adaptive-step sampler run to completion, then the call timed alone
+    thr = None
+    if not args.only_attn:
+        rng = np.random.Generator(np.random.PCG64(lp.seed + 100))
+        blk = workloads.make_peaked_block(rng, B, S, V, seed=lp.seed + 100)
+        pk = [dev_t(workloads.peaked_logits(rng, blk, s)) for s in range(4)]
+        nst = torch.zeros(B, dtype=torch.int32, device=dev)
+        mask.copy_(ones)
+        sampler_steps = 0
+        while sampler_steps < 16 and int(mask.sum().item()) > 0:
+            tt.tt_unmask_threshold(pk[sampler_steps % len(pk)], mask, 0.8, ids, com, None, nst,
+                                   tt.TT_UNMASK_UPDATE_MASK, uws)
+            sampler_steps += 1
+        steps_per_seq = nst.cpu().numpy()
+        mask.copy_(ones)
+        torch.cuda.synchronize()
+        u0.record(stream)
+        for it in range(n_un):
+            tt.tt_unmask_threshold(pk[it % len(pk)], mask, 0.8, ids, com, None, None, 0, uws)
+        u1.record(stream)
+        torch.cuda.synchronize()
+        th_s = u0.elapsed_time(u1) / 1e3 / n_un
+        th_gbs = B * S * V * 4 / th_s / 1e9
+        thr = {"us_per_call": th_s * 1e6, "GB/s": th_gbs, "frac_hbm": th_gbs / HBM_PEAK_GBS,
+               "gamma": 0.8, "sampler_steps_to_resolve_batch": sampler_steps,
+               "mean_steps_per_sequence": float(steps_per_seq.mean()),
+               "max_steps_per_sequence": int(steps_per_seq.max()),
+               "logits": "N(0, 3^2) fp32 [512, 131072] plus one seeded spike per row (peaked)"}
+        log("threshold unmask: %.1f us/call, %.0f GB/s; sampler resolved the batch in %d steps "
+            "(mean %.2f per sequence)" % (th_s * 1e6, th_gbs, sampler_steps, steps_per_seq.mean()))
     if args.only_attn:
         # calibration for FETCH_SIZE / WRITE_SIZE: a plain device copy of 256 MiB
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -309,15 +341,22 @@ def main():
         log("attention algorithmic bytes per launch: %d" % attn_bytes)
         return
 
-    # ---- CPU oracle on a bounded sample of the same workload
+    # ---- CPU oracle on a bounded sample of the same workload: one denoise
+    # step's attention (all 6 layers) for as many sequences as fit about 10 s
+    # on this host, plus their unmask rows, scaled to the whole batch
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        nseq = 2
-        order = np.argsort(lens)
-        sample = sorted({int(order[len(order) // 2]), int(order[len(order) // 2 + 1])})[:nseq]
-        rows = [(b, t, h) for b in sample for t in range(S) for h in range(lp.Hq)]
         threads = oracle.num_threads()
+        order = np.argsort(lens)
+        probe = int(order[len(order) // 2])
+        c0 = time.perf_counter()
+        oracle.block_attn(lp.pools[0], rows=[(probe, t, h) for t in range(S) for h in range(lp.Hq)],
+                          q=lp.q[0][0], k_blk=lp.k_blk[0][0], v_blk=lp.v_blk[0][0])
+        per_seq_layer = time.perf_counter() - c0
+        nseq = int(min(B, max(2, 10.0 / max(per_seq_layer * NL, 1e-3))))
+        sample = sorted(int(order[(len(order) - nseq) // 2 + j]) for j in range(nseq))
+        rows = [(b, t, h) for b in sample for t in range(S) for h in range(lp.Hq)]
         c0 = time.perf_counter()
         for i in range(NL):
             oracle.block_attn(lp.pools[i], rows=rows, q=lp.q[0][i], k_blk=lp.k_blk[0][i],
@@ -331,12 +370,13 @@ def main():
         tok_all = int((lens + S).sum())
         step_s = c_attn * tok_all / tok_sample + c_un * B / len(sample)
         cpu = {"value": 1.0 / step_s, "unit": "denoise-steps/s", "cores": threads, "kind": "oracle",
-               "sample": ("fp64 C oracle (OpenMP, %d threads): step-0 attention of %d sequences "
-                          "(L=%s) over all 6 layers (%d query rows) plus their unmask rows, %.1f s; "
-                          "scaled to the whole batch by context tokens (attention) and rows (unmask)"
-                          % (threads, len(sample), [int(lens[b]) for b in sample], len(rows) * NL,
+               "sample": ("fp64 C oracle (OpenMP, %d threads): step-0 attention of %d of %d "
+                          "sequences (mean L=%.0f) over all 6 layers (%d query rows) plus their "
+                          "unmask rows, %.1f s; scaled to the whole batch by context tokens "
+                          "(attention) and rows (unmask)"
+                          % (threads, len(sample), B, float(lens[sample].mean()), len(rows) * NL,
                              c_attn + c_un))}
-        log("cpu oracle: %.2f s per denoise step (extrapolated)" % step_s)
+        log("cpu oracle: %.2f s per denoise step (extrapolated from %.1f s)" % (step_s, c_attn + c_un))
 
     steps_per_s = T / block_s
     traffic = read_traffic(attn_bytes)
@@ -366,6 +406,7 @@ def main():
                      "tflops": attn_tfs, "mfma_frac": attn_tfs / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
         "unmask": {"us_per_call": un_s * 1e6, "GB/s": un_gbs, "frac_hbm": un_gbs / HBM_PEAK_GBS},
+        "unmask_threshold": thr,
     }
     print(json.dumps(res), flush=True)
 
