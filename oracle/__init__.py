@@ -61,6 +61,8 @@ def _load():
         lib.tto_block_attn.argtypes = [I, I, I, I, I, I, I, I, ctypes.c_double, I,
                                        P, P, P, P, P, P, P, I, P, P, P]
         lib.tto_block_attn.restype = I
+        lib.tto_chunk_attn.argtypes = lib.tto_block_attn.argtypes
+        lib.tto_chunk_attn.restype = I
         lib.tto_unmask.argtypes = [I, I, I, P, P, P, I, P, P, P]
         lib.tto_unmask.restype = I
         lib.tto_unmask_threshold.argtypes = [I, I, I, P, P, ctypes.c_double, P, P, P, P]
@@ -104,8 +106,9 @@ def _c(a, dtype=None):
 
 def block_attn(c, rows: Optional[Sequence[Sequence[int]]] = None, with_wsum: bool = False,
                q=None, k_blk=None, v_blk=None, k_pages=None, v_pages=None,
-               ctx_lens=None, page_table=None):
-    """fp64 block attention.
+               ctx_lens=None, page_table=None, causal: bool = False):
+    """fp64 block attention (``causal``: the context tower's chunk ingest, where
+    chunk position t sees chunk tokens 0..t only).
 
     ``c`` carries the shapes and arrays (any object with the attribute names
     used by ``workloads.AttnCase``); keyword arrays override its fields.
@@ -132,11 +135,12 @@ def block_attn(c, rows: Optional[Sequence[Sequence[int]]] = None, with_wsum: boo
         n = rows_arr.shape[0]
         out = np.zeros((n, D), dtype=np.float64)
         ws = np.zeros((n,), dtype=np.float64) if with_wsum else None
-    err = _load().tto_block_attn(B, S, Hq, c.Hkv, D, c.page_size, page_table.shape[1],
-                                 k_pages.shape[0], float(c.scale), is_bf16,
-                                 _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_pages),
-                                 _ptr(v_pages), _ptr(page_table), _ptr(ctx_lens), n,
-                                 _ptr(rows_arr), _ptr(out), _ptr(ws))
+    fn = _load().tto_chunk_attn if causal else _load().tto_block_attn
+    err = fn(B, S, Hq, c.Hkv, D, c.page_size, page_table.shape[1],
+             k_pages.shape[0], float(c.scale), is_bf16,
+             _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_pages),
+             _ptr(v_pages), _ptr(page_table), _ptr(ctx_lens), n,
+             _ptr(rows_arr), _ptr(out), _ptr(ws))
     if err:
         raise ValueError("oracle block_attn failed with code %d" % err)
     return (out, ws) if with_wsum else out

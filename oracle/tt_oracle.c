@@ -62,17 +62,25 @@ static double elem(const void *base, size_t idx, int is_bf16) {
  * concatenation (context first, then the S block tokens), with no mask: every
  * block query sees all committed context tokens and all S block tokens.
  * GQA: query head h reads KV head h / (Hq / Hkv).
+ *
+ * causal != 0 is the context tower ingesting a committed chunk of S tokens
+ * ([REVIEW, "The idea: freeze the reader, train the writer"]: the frozen
+ * context tower runs causally over clean tokens, and ingests a committed
+ * block as one clean forward chunk, updating its caches): chunk position t
+ * attends over the committed context and chunk tokens 0..t only, so the
+ * concatenation for that row ends at chunk token t.
  */
 static int attn_row(int S, int Hq, int Hkv, int D, int page_size, int max_pages,
                     int num_pages, double scale, int is_bf16, const void *q,
                     const void *k_blk, const void *v_blk, const void *k_pages,
                     const void *v_pages, const int32_t *page_table,
-                    const int32_t *ctx_lens, int b, int t, int h, double *out,
+                    const int32_t *ctx_lens, int b, int t, int h, int causal, double *out,
                     double *wsum) {
   const int g = Hq / Hkv;
   const int hk = h / g;
   const int L = ctx_lens[b];
-  const int N = L + S;
+  const int Sk = causal ? t + 1 : S;   /* block/chunk tokens in the concatenation */
+  const int N = L + Sk;
   if (L < 0 || L > max_pages * page_size) return TTO_ERR_PAGE;
 
   /* 1. the explicit concatenation Kcat = [K_ctx ; K_blk], Vcat likewise */
@@ -91,7 +99,7 @@ static int attn_row(int S, int Hq, int Hkv, int D, int page_size, int max_pages,
           elem(v_pages, (((size_t)page * Hkv + hk) * D + d) * page_size + off, is_bf16);
     }
   }
-  for (int j = 0; j < S; ++j)
+  for (int j = 0; j < Sk; ++j)
     for (int d = 0; d < D; ++d) {
       const size_t src = (((size_t)b * S + j) * Hkv + hk) * D + d;
       kc[(size_t)(L + j) * D + d] = elem(k_blk, src, is_bf16);
@@ -123,17 +131,12 @@ static int attn_row(int S, int Hq, int Hkv, int D, int page_size, int max_pages,
   return TTO_OK;
 }
 
-/*
- * Block attention over rows.  rows == NULL: all B*S*Hq rows, out is
- * [B, S, Hq, D].  Otherwise rows holds n_rows triples (b, t, h) and out is
- * [n_rows, D].  wsum (optional, per row) receives sum_j p_j / Z.
- */
-int tto_block_attn(int B, int S, int Hq, int Hkv, int D, int page_size,
-                   int max_pages, int num_pages, double scale, int is_bf16,
-                   const void *q, const void *k_blk, const void *v_blk,
-                   const void *k_pages, const void *v_pages,
-                   const int32_t *page_table, const int32_t *ctx_lens,
-                   int n_rows, const int32_t *rows, double *out, double *wsum) {
+static int attn_rows(int B, int S, int Hq, int Hkv, int D, int page_size,
+                     int max_pages, int num_pages, double scale, int is_bf16,
+                     const void *q, const void *k_blk, const void *v_blk,
+                     const void *k_pages, const void *v_pages,
+                     const int32_t *page_table, const int32_t *ctx_lens,
+                     int n_rows, const int32_t *rows, int causal, double *out, double *wsum) {
   if (B < 0 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || page_size < 1 ||
       max_pages < 1)
     return TTO_ERR_ARG;
@@ -148,7 +151,7 @@ int tto_block_attn(int B, int S, int Hq, int Hkv, int D, int page_size,
     if (b < 0 || b >= B || t < 0 || t >= S || h < 0 || h >= Hq) e = TTO_ERR_ARG;
     else
       e = attn_row(S, Hq, Hkv, D, page_size, max_pages, num_pages, scale, is_bf16, q,
-                   k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, b, t, h,
+                   k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, b, t, h, causal,
                    out + (size_t)r * D, wsum ? wsum + r : NULL);
     if (e) {
 #pragma omp critical
@@ -156,6 +159,33 @@ int tto_block_attn(int B, int S, int Hq, int Hkv, int D, int page_size,
     }
   }
   return err;
+}
+
+/*
+ * Block attention over rows.  rows == NULL: all B*S*Hq rows, out is
+ * [B, S, Hq, D].  Otherwise rows holds n_rows triples (b, t, h) and out is
+ * [n_rows, D].  wsum (optional, per row) receives sum_j p_j / Z.
+ */
+int tto_block_attn(int B, int S, int Hq, int Hkv, int D, int page_size,
+                   int max_pages, int num_pages, double scale, int is_bf16,
+                   const void *q, const void *k_blk, const void *v_blk,
+                   const void *k_pages, const void *v_pages,
+                   const int32_t *page_table, const int32_t *ctx_lens,
+                   int n_rows, const int32_t *rows, double *out, double *wsum) {
+  return attn_rows(B, S, Hq, Hkv, D, page_size, max_pages, num_pages, scale, is_bf16, q, k_blk,
+                   v_blk, k_pages, v_pages, page_table, ctx_lens, n_rows, rows, 0, out, wsum);
+}
+
+/* Causal chunk ingest: as tto_block_attn, chunk position t seeing chunk
+ * tokens 0..t only (see attn_row). */
+int tto_chunk_attn(int B, int S, int Hq, int Hkv, int D, int page_size,
+                   int max_pages, int num_pages, double scale, int is_bf16,
+                   const void *q, const void *k_blk, const void *v_blk,
+                   const void *k_pages, const void *v_pages,
+                   const int32_t *page_table, const int32_t *ctx_lens,
+                   int n_rows, const int32_t *rows, double *out, double *wsum) {
+  return attn_rows(B, S, Hq, Hkv, D, page_size, max_pages, num_pages, scale, is_bf16, q, k_blk,
+                   v_blk, k_pages, v_pages, page_table, ctx_lens, n_rows, rows, 1, out, wsum);
 }
 
 /*

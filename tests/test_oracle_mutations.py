@@ -39,6 +39,9 @@ MUTATIONS = [
      "if (best < 0 || conf[r] >= conf[(size_t)b * S + best]) best = t;"),
     ("threshold_ignores_mask", "      if (!mask[r]) continue;\n      ++n;", "      ++n;"),
     ("nsteps_counts_empty", "if (nsteps && n > 0) nsteps[b] += 1;", "if (nsteps) nsteps[b] += 1;"),
+    ("chunk_excludes_self", "const int Sk = causal ? t + 1 : S;", "const int Sk = causal ? t : S;"),
+    ("chunk_not_causal", "const int Sk = causal ? t + 1 : S;", "const int Sk = S;"),
+    ("chunk_anticausal", "const int Sk = causal ? t + 1 : S;", "const int Sk = causal ? S - t : S;"),
 ]
 
 
@@ -85,6 +88,8 @@ def _pins_pass():
                 return False
         if not _threshold_pins_pass():
             return False
+        if not _chunk_pins_pass():
+            return False
     except ValueError:
         return False
     return True
@@ -95,6 +100,19 @@ def _threshold_pins_pass():
     checks = [T.test_hand_sequence_by_gamma, T.test_hand_fallback_tie, T.test_hand_empty_mask,
               T.test_hand_adaptive_loop, T.test_loop_budget_stops_unresolved_blocks]
     checks += [lambda: T.test_gamma_one_is_top1(0), lambda: T.test_negative_gamma_commits_every_masked(0)]
+    for f in checks:
+        try:
+            f()
+        except AssertionError:
+            return False
+    return True
+
+
+def _chunk_pins_pass():
+    import test_oracle_chunk as C
+    checks = [lambda case=case: C.test_hand_cases(case) for case in C.G["cases"]]
+    checks += [lambda: C.test_against_masked_sdpa([21, 0, 40], 4, 8, 2, 16),
+               C.test_future_chunk_tokens_do_not_matter]
     for f in checks:
         try:
             f()
