@@ -124,6 +124,25 @@ int tt_block_attn(const tt_attn_desc *desc, const void *q, const void *k_blk,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Causal chunk ingest by the context tower ("The idea: freeze the reader,
+ * train the writer", paperfeed review: the frozen context tower runs
+ * causally over clean tokens and ingests a committed block as one clean
+ * forward chunk, updating its caches).  Same arguments, layouts, workspace
+ * (tt_block_attn_workspace_bytes) and precision as tt_block_attn, with one
+ * difference: chunk position t attends over the L_b committed tokens and
+ * chunk tokens 0..t only,
+ *
+ *   O[b,t,h,:] = softmax_j( scale * q[b,t,h,:] . Kcat_j ) @ Vcat,
+ *   Kcat = [K_ctx(b, 0..L_b-1) ; k_blk(b, 0..t)],  Vcat likewise.
+ *
+ * Follow it with tt_kv_append of the same chunk to grow the caches.
+ */
+int tt_chunk_attn(const tt_attn_desc *desc, const void *q, const void *k_blk,
+                  const void *v_blk, const void *k_pages, const void *v_pages,
+                  const int32_t *page_table, const int32_t *ctx_lens, void *out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Block commit: the context cache ingests a resolved block ("The idea: freeze
  * the reader, train the writer", paperfeed review: once a block is resolved
  * it is committed and the context tower's caches are updated).  For every

@@ -66,11 +66,12 @@ class DevCase:
         c = self.c
         return torch.full((c.B, c.S, c.Hq, c.D), float("nan"), dtype=self.el, device="cuda")
 
-    def attn(self, out=None, q=None, k_blk=None, v_blk=None):
+    def attn(self, out=None, q=None, k_blk=None, v_blk=None, causal=False):
         import two_tower_attention_amd as tt
         out = self.new_out() if out is None else out
         self.ws.fill_(0xFF)   # NaN-poison the workspace: partials must be written before use
-        tt.tt_block_attn(self.desc, self.q if q is None else q,
+        fn = tt.tt_chunk_attn if causal else tt.tt_block_attn
+        fn(self.desc, self.q if q is None else q,
                          self.k_blk if k_blk is None else k_blk,
                          self.v_blk if v_blk is None else v_blk, self.k_pages, self.v_pages,
                          self.page_table, self.ctx_lens, out, self.ws)

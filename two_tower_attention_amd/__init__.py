@@ -23,7 +23,7 @@ TT_BF16 = 0
 TT_F32 = 1
 TT_UNMASK_UPDATE_MASK = 1
 
-EXPORTS = ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_kv_append",
+EXPORTS = ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_chunk_attn", "tt_kv_append",
            "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold", "tt_status_str",
            "tt_last_error", "tt_abi_version")
 
@@ -63,6 +63,7 @@ def load_library(path: Optional[str] = None):
     DP = ctypes.POINTER(AttnDesc)
     lib.tt_block_attn_workspace_bytes.argtypes = [DP, ctypes.POINTER(SZ)]
     lib.tt_block_attn.argtypes = [DP, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.tt_chunk_attn.argtypes = [DP, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.tt_kv_append.argtypes = [DP, P, P, P, P, P, P, P]
     lib.tt_unmask_workspace_bytes.argtypes = [I32, I32, I32, ctypes.POINTER(SZ)]
     lib.tt_unmask.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, ctypes.c_uint32, P, SZ, P]
@@ -146,6 +147,19 @@ def tt_block_attn_workspace_bytes(desc: AttnDesc) -> int:
 
 def tt_block_attn(desc: AttnDesc, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens,
                   out, workspace=None, stream=None) -> None:
+    _attn("tt_block_attn", desc, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, out,
+          workspace, stream)
+
+
+def tt_chunk_attn(desc: AttnDesc, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens,
+                  out, workspace=None, stream=None) -> None:
+    """Causal chunk ingest (see include/tt.h); same arguments as tt_block_attn."""
+    _attn("tt_chunk_attn", desc, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, out,
+          workspace, stream)
+
+
+def _attn(name, desc, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, out, workspace,
+          stream):
     torch = _torch()
     el = _el(desc)
     B, S, Hq, Hkv, D = desc.batch, desc.block, desc.heads_q, desc.heads_kv, desc.head_dim
@@ -160,7 +174,7 @@ def tt_block_attn(desc: AttnDesc, q, k_blk, v_blk, k_pages, v_pages, page_table,
             _ptr(ctx_lens, "ctx_lens", torch.int32, B), _ptr(out, "out", el, B * S * Hq * D)]
     ws = _ptr(workspace, "workspace", allow_none=True)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().tt_block_attn(ctypes.byref(desc), *args, ws, nbytes, _stream(stream)))
+    _check(getattr(load_library(), name)(ctypes.byref(desc), *args, ws, nbytes, _stream(stream)))
 
 
 def tt_kv_append(desc: AttnDesc, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens,

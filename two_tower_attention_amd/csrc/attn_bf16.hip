@@ -79,6 +79,7 @@ struct Params {
   __bf16 *ws_o; // [2G][D*256] partial O^T / l (bf16)
   float *ws_ml;  // [2G][256][2]  (reference max in log2 units, sum l)
   int B, S, Hq, Hkv, g, page_size, lps, max_pages, num_pages, max_ctx, qchunks, G;
+  int causal;  // chunk ingest: block position t sees block keys 0..t only
   float sl2;
 };
 
@@ -195,20 +196,20 @@ __device__ __forceinline__ void lds_barrier() {
 // vmcnt-only s_waitcnt immediate (gfx9 encoding; expcnt/lgkmcnt left at max).
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
-// Which waves issue the direct loads.  kIssuer 0: every wave issues its own
-// share of a tile when its compute starts; 1: each lead wave w issues its
-// share and that of its lag partner w + waves/2 when its compute starts;
-// 2: each lag wave issues both shares when its compute ends, where it would
-// otherwise wait at the barrier for the lead wave; 3: every wave issues its
-// own share, lead waves when their compute starts, lag waves when it ends.
+// Which waves issue the direct loads of a tile, at the start of their
+// compute.  kIssuer 0: every wave its own share; 1: each lead wave w its
+// share and that of its lag partner w + waves/2.  Issuing blocks a wave
+// while the memory queue is full; with 1 the lag waves, which carry the
+// longer compute, never block.  (Issuing later in the tile, or from the lag
+// waves, measured slower.)
 #ifndef TT_ATTN_ISSUER
 #define TT_ATTN_ISSUER 1
 #endif
 constexpr int kIssuer = TT_ATTN_ISSUER;
-#define TT_ATTN_ISSUE ((kIssuer == 0 || kIssuer == 3) ? 1 : 2)
+#define TT_ATTN_ISSUE (kIssuer == 0 ? 1 : 2)
 constexpr int kIssue = TT_ATTN_ISSUE;
 constexpr int kWaves = kThreads / 64;
-static_assert(kIssuer >= 0 && kIssuer <= 3, "issuer mode");
+static_assert(kIssuer == 0 || kIssuer == 1, "issuer mode");
 
 // Wait until at most `tiles_after` tiles' worth of this wave's direct loads
 // are in flight.
@@ -252,10 +253,8 @@ __device__ __forceinline__ void value_slot(int iw, int n, int &d, int &c) {
   c = (slot & 7) ^ ((d & 7) ^ ((d >> 3) & 1));
 }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-// Index of this wave among the issuing waves.
-__device__ __forceinline__ int issuer_id() {
-  return kIssuer == 2 ? wave_id() - kWaves / 2 : wave_id();
-}
+// Index of this wave among the issuing waves (the lead waves come first).
+__device__ __forceinline__ int issuer_id() { return wave_id(); }
 // Positions past the context are clamped to a valid token: keys there are
 // masked by score, values are zeroed in LDS before use.
 __device__ __forceinline__ int key_pos(const Unit &u, int i, int t) {
@@ -538,13 +537,15 @@ __device__ __forceinline__ void mfma_pv(const Batch &x, int b, const PTile<D> &P
 
 // Online softmax of a tile's scores (log2 domain): rescales the accumulators
 // when the running max grows by more than 2^kLazy, returns P in bf16.
+// Keys at or past klim (per lane: the lane's query row) are masked when
+// `mask` (wave-uniform) is set.
 template <int D>
-__device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2], int nvalid,
+__device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2], int klim, bool mask,
                                              Acc<D> &A, PTile<D> &P) {
   const int hl = (threadIdx.x & 63) >> 5;
   // key of register r of half tb in lane half hl: 32*tb + 16*(r/8) + 8*hl + r%8
-  if (nvalid < kTile) {
-    const int lim = nvalid - 8 * hl;
+  if (mask) {
+    const int lim = klim - 8 * hl;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -628,15 +629,15 @@ __device__ __forceinline__ void pv_phase(const unsigned char *stage, const unsig
 // Lead role, whole tile: scores -> softmax -> P.V.  The first value batch is
 // read under the last score MFMAs and lands during the softmax.
 template <int D, typename Loads>
-__device__ __forceinline__ void tile_lead(const Params &p, const unsigned char *stage, int nvalid,
-                                          const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
+__device__ __forceinline__ void tile_lead(const Params &p, const unsigned char *stage, int klim,
+                                          bool mask, const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
                                           PTile<D> &P, const Loads &ld) {
   Batch buf[2];
   f32x16 s[2];
   ld.issue();
   read_qk<D>(stage, 0, buf[0]);
   score_phase<D, true>(stage, qr, s, buf);
-  softmax_tile<D>(p, s, nvalid, A, P);
+  softmax_tile<D>(p, s, klim, mask, A, P);
   sched_fence();
   pv_phase<D, false, false>(stage, nullptr, P, A, buf);
 }
@@ -651,18 +652,14 @@ __device__ __forceinline__ void tile_lag(const Params &p, const unsigned char *p
                                          const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
                                          PTile<D> &P, Batch (&buf)[2], const Loads &ld) {
   f32x16 s[2];
-  if (kIssuer < 2) ld.issue();
+  ld.issue();
   if (FIRST) {
     read_qk<D>(stage, 0, buf[0]);
   } else {
     pv_phase<D, true, true>(prev, stage, P, A, buf);
   }
   score_phase<D, true>(stage, qr, s, buf);
-  softmax_tile<D>(p, s, nvalid, A, P);
-  if (kIssuer >= 2) {
-    sched_fence();
-    ld.issue();
-  }
+  softmax_tile<D>(p, s, nvalid, nvalid < kTile, A, P);
 }
 
 // Start of context tile i of a sub-range [c0, c1): waits for the tile and
@@ -702,7 +699,7 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
     // the lag waves issue no loads when their lead partners carry them
-    constexpr bool kIssues = kIssuer == 0 || kIssuer == 3 || (kIssuer == 1) == !LAG;
+    constexpr bool kIssues = kIssuer == 0 || !LAG;
     TilePages<D, BIG> pg;
     if (kIssues) {
 #pragma unroll
@@ -723,7 +720,7 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
     if (!LAG) {
       for (int i = c0; i < c1; ++i) {
         const unsigned char *stage = begin_tile<D>(u, i, c0, c1, ring, nvalid);
-        tile_lead<D>(p, stage, nvalid, qr, A, P, loads(i));
+        tile_lead<D>(p, stage, nvalid, nvalid < kTile, qr, A, P, loads(i));
       }
     } else {
       // the first tile has no predecessor; the last one's P.V drains after the loop
@@ -793,7 +790,10 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
     unsigned char *stage = ring;
     stage_block_tile<D>(p, u, stage);
     lds_barrier();
-    tile_lead<D>(p, stage, p.S, qr, A, P, NoLoads{});
+    // chunk ingest: the lane's query row (block position t) sees keys 0..t
+    const int qt = (u.qc * kQRows + wave * 32 + ln) / p.g;
+    const int klim = p.causal ? min(p.S, qt + 1) : p.S;
+    tile_lead<D>(p, stage, klim, p.causal || p.S < kTile, qr, A, P, NoLoads{});
     lds_barrier();
   }
 
@@ -1037,8 +1037,9 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus) {
 hipError_t launch_attn_bf16(const AttnPlan &pl, const void *q, const void *k_blk,
                             const void *v_blk, const void *k_pages, const void *v_pages,
                             const int32_t *page_table, const int32_t *ctx_lens, void *out,
-                            void *workspace, hipStream_t stream) {
+                            void *workspace, int causal, hipStream_t stream) {
   Params prm;
+  prm.causal = causal;
   prm.q = (const __bf16 *)q; prm.k_blk = (const __bf16 *)k_blk; prm.v_blk = (const __bf16 *)v_blk;
   prm.k_pages = (const __bf16 *)k_pages; prm.v_pages = (const __bf16 *)v_pages;
   prm.page_table = page_table; prm.ctx_lens = ctx_lens;

@@ -15,6 +15,7 @@ struct F32Params {
   const int32_t *page_table, *ctx_lens;
   float *out;
   int B, S, Hq, Hkv, g, D, page_size, max_pages, num_pages, max_ctx;
+  int causal;  // chunk ingest: block position t sees block keys 0..t only
   float scale;
 };
 
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
   const int b = row / (p.S * p.Hq), t = (row / p.Hq) % p.S, h = row % p.Hq;
   const int hk = h / p.g;
   const int L = min(max(p.ctx_lens[b], 0), p.max_ctx);
-  const int N = L + p.S;
+  const int N = L + (p.causal ? t + 1 : p.S);  // context, then the visible block keys
   const int32_t *pt = p.page_table + (size_t)b * p.max_pages;
   const float *qrow = p.q + (((size_t)b * p.S + t) * p.Hq + h) * p.D;
   for (int d = lane; d < p.D; d += 64) qs[d] = qrow[d];
@@ -106,8 +107,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Params p) {
 hipError_t launch_attn_f32(const tt_attn_desc &d, float scale, const float *q,
                            const float *k_blk, const float *v_blk, const float *k_pages,
                            const float *v_pages, const int32_t *page_table,
-                           const int32_t *ctx_lens, float *out, hipStream_t stream) {
+                           const int32_t *ctx_lens, float *out, int causal, hipStream_t stream) {
   F32Params p;
+  p.causal = causal;
   p.q = q; p.k_blk = k_blk; p.v_blk = v_blk; p.k_pages = k_pages; p.v_pages = v_pages;
   p.page_table = page_table; p.ctx_lens = ctx_lens; p.out = out;
   p.B = d.batch; p.S = d.block; p.Hq = d.heads_q; p.Hkv = d.heads_kv;

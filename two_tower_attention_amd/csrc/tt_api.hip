@@ -130,10 +130,10 @@ int tt_block_attn_workspace_bytes(const tt_attn_desc *d, size_t *bytes) {
   return ok();
 }
 
-int tt_block_attn(const tt_attn_desc *d, const void *q, const void *k_blk, const void *v_blk,
-                  const void *k_pages, const void *v_pages, const int32_t *page_table,
-                  const int32_t *ctx_lens, void *out, void *workspace, size_t workspace_bytes,
-                  void *stream) {
+static int block_attn(const tt_attn_desc *d, const void *q, const void *k_blk, const void *v_blk,
+                      const void *k_pages, const void *v_pages, const int32_t *page_table,
+                      const int32_t *ctx_lens, void *out, void *workspace, size_t workspace_bytes,
+                      int causal, void *stream) {
   int st = check_desc(d);
   if (st) return st;
   if (d->batch == 0) return ok();
@@ -158,15 +158,31 @@ int tt_block_attn(const tt_attn_desc *d, const void *q, const void *k_blk, const
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned(workspace, 16)) return fail(TT_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
     e = tt::launch_attn_bf16(plan, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, out,
-                             workspace, s);
+                             workspace, causal, s);
   } else {
     const float scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
     e = tt::launch_attn_f32(*d, scale, (const float *)q, (const float *)k_blk,
                             (const float *)v_blk, (const float *)k_pages, (const float *)v_pages,
-                            page_table, ctx_lens, (float *)out, s);
+                            page_table, ctx_lens, (float *)out, causal, s);
   }
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int tt_block_attn(const tt_attn_desc *d, const void *q, const void *k_blk, const void *v_blk,
+                  const void *k_pages, const void *v_pages, const int32_t *page_table,
+                  const int32_t *ctx_lens, void *out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+  return block_attn(d, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, out, workspace,
+                    workspace_bytes, 0, stream);
+}
+
+int tt_chunk_attn(const tt_attn_desc *d, const void *q, const void *k_blk, const void *v_blk,
+                  const void *k_pages, const void *v_pages, const int32_t *page_table,
+                  const int32_t *ctx_lens, void *out, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+  return block_attn(d, q, k_blk, v_blk, k_pages, v_pages, page_table, ctx_lens, out, workspace,
+                    workspace_bytes, 1, stream);
 }
 
 int tt_kv_append(const tt_attn_desc *d, const void *k_blk, const void *v_blk, void *k_pages,

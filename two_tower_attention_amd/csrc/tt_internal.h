@@ -34,12 +34,12 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus);
 hipError_t launch_attn_bf16(const AttnPlan &p, const void *q, const void *k_blk,
                             const void *v_blk, const void *k_pages, const void *v_pages,
                             const int32_t *page_table, const int32_t *ctx_lens, void *out,
-                            void *workspace, hipStream_t stream);
+                            void *workspace, int causal, hipStream_t stream);
 
 hipError_t launch_attn_f32(const tt_attn_desc &d, float scale, const float *q,
                            const float *k_blk, const float *v_blk, const float *k_pages,
                            const float *v_pages, const int32_t *page_table,
-                           const int32_t *ctx_lens, float *out, hipStream_t stream);
+                           const int32_t *ctx_lens, float *out, int causal, hipStream_t stream);
 
 hipError_t launch_kv_append(const tt_attn_desc &d, const void *k_blk, const void *v_blk,
                             void *k_pages, void *v_pages, const int32_t *page_table,
