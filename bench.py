@@ -277,6 +277,17 @@ def main():
     a1.record(stream)
     torch.cuda.synchronize()
     attn_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
+    # the context tower's causal chunk ingest on the same inputs
+    chunk_s = None
+    if not args.only_attn:
+        a0.record(stream)
+        for it in range(args.attn_iters):
+            s_, i_ = (it // NL) % T, it % NL
+            tt.tt_chunk_attn(desc, q[s_][i_], kb[s_][i_], vb[s_][i_], kp[i_], vp[i_], pt[i_], ctx[i_],
+                             out[i_], ws)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        chunk_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
     lens = p0.ctx_lens.astype(np.int64)
     kv_bytes = int(lens.sum()) * lp.Hkv * lp.D * 2 * 2
     qo_bytes = 2 * B * S * lp.Hq * lp.D * 2
@@ -286,6 +297,12 @@ def main():
     attn_gbs = attn_bytes / attn_s / 1e9
     attn_tfs = attn_flops / attn_s / 1e12
     log("attention: %.1f us/launch, %.0f GB/s, %.0f TFLOP/s" % (attn_s * 1e6, attn_gbs, attn_tfs))
+    chunk = None
+    if chunk_s is not None:
+        chunk = {"us_per_launch": chunk_s * 1e6, "GB/s": attn_bytes / chunk_s / 1e9,
+                 "frac_hbm": attn_bytes / chunk_s / 1e9 / HBM_PEAK_GBS,
+                 "workload": "causal chunk ingest of the 16-token block, same layer inputs"}
+        log("chunk ingest: %.1f us/launch, %.0f GB/s" % (chunk_s * 1e6, chunk["GB/s"]))
 
     # ---- unmask alone (flags 0: the all-masked state is left untouched)
     mask.copy_(ones)
@@ -342,7 +359,7 @@ def main():
         return
 
     # ---- CPU oracle on a bounded sample of the same workload: one denoise
-    # step's attention (all 6 layers) for as many sequences as fit about 10 s
+    # step's attention (all 6 layers) for as many sequences as fit about 20 s
     # on this host, plus their unmask rows, scaled to the whole batch
     cpu = None
     if not args.no_cpu_baseline:
@@ -354,7 +371,7 @@ def main():
         oracle.block_attn(lp.pools[0], rows=[(probe, t, h) for t in range(S) for h in range(lp.Hq)],
                           q=lp.q[0][0], k_blk=lp.k_blk[0][0], v_blk=lp.v_blk[0][0])
         per_seq_layer = time.perf_counter() - c0
-        nseq = int(min(B, max(2, 10.0 / max(per_seq_layer * NL, 1e-3))))
+        nseq = int(min(B, max(2, 20.0 / max(per_seq_layer * NL, 1e-3))))
         sample = sorted(int(order[(len(order) - nseq) // 2 + j]) for j in range(nseq))
         rows = [(b, t, h) for b in sample for t in range(S) for h in range(lp.Hq)]
         c0 = time.perf_counter()
@@ -407,6 +424,7 @@ def main():
         "cpu_baseline": cpu,
         "unmask": {"us_per_call": un_s * 1e6, "GB/s": un_gbs, "frac_hbm": un_gbs / HBM_PEAK_GBS},
         "unmask_threshold": thr,
+        "chunk_attn": chunk,
     }
     print(json.dumps(res), flush=True)
 
