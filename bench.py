@@ -304,6 +304,42 @@ def main():
                  "workload": "causal chunk ingest of the 16-token block, same layer inputs"}
         log("chunk ingest: %.1f us/launch, %.0f GB/s" % (chunk_s * 1e6, chunk["GB/s"]))
 
+    # ---- sampling block sizes: one attention launch per layer at S = 8, 32,
+    # 64 over the same context pools (the pages' block-size knob)
+    block_sizes = None
+    if not args.only_attn:
+        block_sizes = {}
+        for S2 in (8, 32, 64):
+            d2 = tt.make_desc(B, S2, lp.Hq, lp.Hkv, lp.D, lp.page_size, p0.page_table.shape[1],
+                              p0.k_pages.shape[0], int(p0.ctx_lens.max()))
+            rng2 = np.random.Generator(np.random.PCG64(lp.seed * 100 + S2))
+            inp = [[dev_bf16(a) for a in workloads.block_inputs(rng2, B, S2, lp.Hq, lp.Hkv, lp.D)]
+                   for _ in range(NL)]
+            o2 = torch.empty((B, S2, lp.Hq, lp.D), dtype=torch.bfloat16, device=dev)
+            ws2 = torch.empty(max(tt.tt_block_attn_workspace_bytes(d2), 16), dtype=torch.uint8,
+                              device=dev)
+            for i in range(NL):
+                tt.tt_block_attn(d2, *inp[i], kp[i], vp[i], pt[i], ctx[i], o2, ws2)
+            torch.cuda.synchronize()
+            n2 = 4 * NL
+            a0.record(stream)
+            for it in range(n2):
+                i = it % NL
+                tt.tt_block_attn(d2, *inp[i], kp[i], vp[i], pt[i], ctx[i], o2, ws2)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            t2 = a0.elapsed_time(a1) / 1e3 / n2
+            by2 = kv_bytes + 2 * B * S2 * lp.Hq * lp.D * 2 + 2 * B * S2 * lp.Hkv * lp.D * 2
+            fl2 = 4 * lp.D * S2 * lp.Hq * int((lens + S2).sum())
+            block_sizes[str(S2)] = {"us_per_launch": t2 * 1e6, "GB/s": by2 / t2 / 1e9,
+                                    "TFLOP/s": fl2 / t2 / 1e12,
+                                    "frac_hbm": by2 / t2 / 1e9 / HBM_PEAK_GBS,
+                                    "frac_mfma": fl2 / t2 / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                    "context_passes": -(-S2 * (lp.Hq // lp.Hkv) // 256)}
+            log("block size %d: %.1f us/launch, %.0f GB/s, %.0f TFLOP/s" % (
+                S2, t2 * 1e6, by2 / t2 / 1e9, fl2 / t2 / 1e12))
+            del inp, o2, ws2
+
     # ---- unmask alone (flags 0: the all-masked state is left untouched)
     mask.copy_(ones)
     u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -425,6 +461,7 @@ def main():
         "unmask": {"us_per_call": un_s * 1e6, "GB/s": un_gbs, "frac_hbm": un_gbs / HBM_PEAK_GBS},
         "unmask_threshold": thr,
         "chunk_attn": chunk,
+        "block_sizes": block_sizes,
     }
     print(json.dumps(res), flush=True)
 

@@ -71,7 +71,9 @@ EDGE = [
     ("pages32", 3, 16, 32, 2, 128, [31, 32, 500], 32),
     ("head64_g4", 3, 16, 8, 2, 64, [48, 0, 333], 64),
     ("mha_g1", 2, 16, 4, 4, 128, [100, 7], 256),
+    ("block8", 3, 8, 32, 2, 128, [0, 90, 1000], 256),
     ("two_query_chunks", 2, 32, 32, 2, 128, [80, 700], 256),
+    ("block64_d128", 2, 64, 32, 2, 128, [64, 777], 256),
     ("four_query_chunks", 1, 64, 32, 2, 64, [129], 128),
     ("odd_block", 3, 5, 6, 3, 64, [17, 0, 90], 16),
     ("many_units", 100, 16, 32, 2, 128, list(range(0, 1000, 10)), 256),

@@ -53,7 +53,10 @@ constexpr int kMinTiles = 8;     // smallest range worth a work-group
 // for the unit's fixed cost (Q load, page-id cache, pipeline fill, block
 // tile, epilogue) so that ranges which cut unit boundaries get fewer real
 // tiles.  A virtual tile holds no work.
-constexpr int kUnitPad = 2;
+#ifndef TT_ATTN_UNITPAD
+#define TT_ATTN_UNITPAD 4
+#endif
+constexpr int kUnitPad = TT_ATTN_UNITPAD;
 constexpr float kLazy = 8.0f;    // rescale when max grows by > 2^kLazy
 
 template <int D>

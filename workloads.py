@@ -92,6 +92,14 @@ def _draw(rng: np.random.Generator, shape, dtype: str, sigma: float = 1.0):
     return bf16_bits(x) if dtype == "bf16" else x
 
 
+def block_inputs(rng: np.random.Generator, B: int, S: int, Hq: int, Hkv: int, D: int,
+                 dtype: str = "bf16"):
+    """Queries and the block's own keys/values, N(0, 1): q [B,S,Hq,D],
+    k_blk and v_blk [B,S,Hkv,D] (bf16 bits or fp32)."""
+    return (_draw(rng, (B, S, Hq, D), dtype), _draw(rng, (B, S, Hkv, D), dtype),
+            _draw(rng, (B, S, Hkv, D), dtype))
+
+
 def make_attn_case(rng: np.random.Generator, *, B: int, S: int, Hq: int, Hkv: int,
                    D: int, ctx_lens, page_size: int, dtype: str = "bf16",
                    extra_tokens: int = 0, shuffle_pages: bool = True,
