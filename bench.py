@@ -152,6 +152,9 @@ def main():
     ap.add_argument("--attn-iters", type=int, default=96, help="launches in the attention-only timing")
     ap.add_argument("--only-attn", action="store_true",
                     help="counter runs: attention launches plus one 256 MiB calibration copy")
+    ap.add_argument("--core", action="store_true",
+                    help="kernel-trace runs: the denoise loop and the attention timing only (no "
+                         "chunk ingest, block sizes, threshold unmask or CPU baseline)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files into a summary")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
@@ -165,6 +168,9 @@ def main():
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats, command=args.profile_command)
         return
+    if args.core:
+        args.no_cpu_baseline = True
+    extras = not (args.only_attn or args.core)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -279,7 +285,7 @@ def main():
     attn_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
     # the context tower's causal chunk ingest on the same inputs
     chunk_s = None
-    if not args.only_attn:
+    if extras:
         a0.record(stream)
         for it in range(args.attn_iters):
             s_, i_ = (it // NL) % T, it % NL
@@ -307,7 +313,7 @@ def main():
     # ---- sampling block sizes: one attention launch per layer at S = 8, 32,
     # 64 over the same context pools (the pages' block-size knob)
     block_sizes = None
-    if not args.only_attn:
+    if extras:
         block_sizes = {}
         for S2 in (8, 32, 64):
             d2 = tt.make_desc(B, S2, lp.Hq, lp.Hkv, lp.D, lp.page_size, p0.page_table.shape[1],
@@ -356,7 +362,7 @@ def main():
     # ---- threshold form of the commit rule (gamma = 0.8) on peaked logits:
     # the adaptive-step sampler run to completion, then the call timed alone
     thr = None
-    if not args.only_attn:
+    if extras:
         rng = np.random.Generator(np.random.PCG64(lp.seed + 100))
         blk = workloads.make_peaked_block(rng, B, S, V, seed=lp.seed + 100)
         pk = [dev_t(workloads.peaked_logits(rng, blk, s)) for s in range(4)]
