@@ -270,14 +270,21 @@ __device__ __forceinline__ int value_pos(const Unit &u, int i, int c) {
 
 // Page ids behind this lane's direct loads of one tile, read from the LDS
 // page-id cache one tile ahead of their use.  With pages of at least one
-// tile (BIG), a tile lies inside one page: one id per tile, wave-uniform.
+// tile (BIG), a tile lies inside one page: one id per tile, wave-uniform,
+// and each lane's byte offsets from the tile's key / value start are the
+// same for every tile (set once by lane_offsets).
 template <int D, bool BIG>
 struct TilePages {
   int k[Share<D>::NK], v[Share<D>::NV];
+  __device__ __forceinline__ void lane_offsets(const Params &) {}
 };
 template <int D>
 struct TilePages<D, true> {
   int pg;
+  // value load n sits (n / 2) * 16 feature rows after load n % 2 (the slot
+  // swizzle depends on n only through n % 2), so two offsets cover them
+  unsigned ko[Share<D>::NK], vo[2];
+  __device__ __forceinline__ void lane_offsets(const Params &p);
 };
 
 template <int D, bool BIG>
@@ -300,6 +307,38 @@ __device__ __forceinline__ void read_pages(const Params &p, const Unit &u, int i
       pg.v[n] = pcache[(value_pos(u, i, c) >> p.lps) - pbase];
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void TilePages<D, true>::lane_offsets(const Params &p) {
+  const int iw = issuer_id();
+#pragma unroll
+  for (int n = 0; n < Share<D>::NK; ++n) {
+    int t, c;
+    key_slot<D>(iw, n, t, c);
+    ko[n] = (unsigned)(t * D + 8 * c) * 2u;
+  }
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    int d, c;
+    value_slot<D>(iw, n, d, c);
+    vo[n] = (unsigned)(d * p.page_size + 8 * c) * 2u;
+  }
+}
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, no stride; loads
+// past `bytes` return zeros instead of touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// One direct load through a buffer descriptor: bytes r + voff + soff ->
+// LDS lds (+ 16 * lane).  The descriptor, soff and the LDS base are scalar
+// per tile; the per-lane offset is fixed, so issuing takes no vector
+// instructions.
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
+                                        unsigned char *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
 }
 
 // One direct load: global `src` -> LDS lds + n KiB (+ 16 * lane).  The
@@ -331,20 +370,16 @@ __device__ __forceinline__ void issue_tile(const Params &p, const Unit &u, int i
     const int page = __builtin_amdgcn_readfirstlane(pg.pg);
     const size_t block = ((size_t)page * p.Hkv + u.h) * p.page_size * D;  // (page, head) block
     const int off = (i * kTile) & pmask;                                   // tile start in the page
-    const __bf16 *kb = p.k_pages + block + (size_t)off * D;
-    const __bf16 *vb = p.v_pages + block + off;
+    // the key tile is contiguous; the value tile is D rows of kTile tokens,
+    // page_size apart
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k_pages + block + (size_t)off * D, G::K_BYTES);
+    const __amdgpu_buffer_rsrc_t rv =
+        buffer_rsrc(p.v_pages + block + off, ((D - 1) * p.page_size + kTile) * 2);
 #pragma unroll
-    for (int n = 0; n < Share<D>::NK; ++n) {
-      int t, c;
-      key_slot<D>(iw, n, t, c);
-      dma(kb + (unsigned)(t * D + 8 * c), kl, n);
-    }
+    for (int n = 0; n < Share<D>::NK; ++n) dma_buf(rk, pg.ko[n], 0u, kl + n * 1024);
 #pragma unroll
-    for (int n = 0; n < Share<D>::NV; ++n) {
-      int d, c;
-      value_slot<D>(iw, n, d, c);
-      dma(vb + (unsigned)(d * p.page_size + 8 * c), vl, n);
-    }
+    for (int n = 0; n < Share<D>::NV; ++n)
+      dma_buf(rv, pg.vo[n & 1], (unsigned)((n >> 1) * 32 * p.page_size), vl + n * 1024);
   } else {
 #pragma unroll
     for (int n = 0; n < Share<D>::NK; ++n) {
@@ -705,6 +740,7 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
     constexpr bool kIssues = kIssuer == 0 || !LAG;
     TilePages<D, BIG> pg;
     if (kIssues) {
+      pg.lane_offsets(p);
 #pragma unroll
       for (int j = 0; j < kAhead; ++j)
         if (c0 + j < c1) {
