@@ -67,6 +67,10 @@ def _load():
         lib.tto_unmask.restype = I
         lib.tto_unmask_threshold.argtypes = [I, I, I, P, P, ctypes.c_double, P, P, P, P]
         lib.tto_unmask_threshold.restype = I
+        lib.tto_lmhead_logits.argtypes = [I, I, I, P, P, P, I, P]
+        lib.tto_lmhead_logits.restype = I
+        lib.tto_unmask_f64.argtypes = [I, I, I, P, P, P, I, P, P, P]
+        lib.tto_unmask_f64.restype = I
         lib.tto_num_threads.argtypes = []
         lib.tto_num_threads.restype = I
         _lib = lib
@@ -162,6 +166,62 @@ def unmask(logits: np.ndarray, mask: np.ndarray, k_commit: Optional[np.ndarray] 
     if err:
         raise ValueError("oracle unmask failed with code %d" % err)
     return ids, commit, conf
+
+
+def lmhead_logits(hidden: np.ndarray, weight: np.ndarray,
+                  rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Exact LM-head logits in fp64: hidden [R, H] and weight [V, H] as bf16
+    bit patterns (uint16); returns [len(rows) or R, V]."""
+    hidden = _c(hidden, np.uint16)
+    weight = _c(weight, np.uint16)
+    R, H = hidden.shape
+    V, H2 = weight.shape
+    if H2 != H:
+        raise ValueError("hidden and weight disagree on the hidden size")
+    sel = None if rows is None else _c(np.asarray(rows, dtype=np.int32), np.int32)
+    n = R if sel is None else sel.shape[0]
+    out = np.zeros((n, V), dtype=np.float64)
+    err = _load().tto_lmhead_logits(R, H, V, _ptr(hidden), _ptr(weight), _ptr(sel), n, _ptr(out))
+    if err:
+        raise ValueError("oracle lmhead_logits failed with code %d" % err)
+    return out
+
+
+def unmask_f64(logits: np.ndarray, mask: np.ndarray, k_commit: Optional[np.ndarray] = None,
+               remaining_steps: int = 1):
+    """The count-form unmask (as unmask()) on fp64 logits [B*S, V]."""
+    mask = _c(mask, np.uint8)
+    B, S = mask.shape
+    logits = _c(logits, np.float64).reshape(B * S, -1)
+    V = logits.shape[1]
+    ids = np.zeros((B, S), dtype=np.int32)
+    commit = np.zeros((B, S), dtype=np.uint8)
+    conf = np.zeros((B, S), dtype=np.float64)
+    kc = None if k_commit is None else _c(k_commit, np.int32).reshape(B)
+    err = _load().tto_unmask_f64(B, S, V, _ptr(logits), _ptr(mask), _ptr(kc),
+                                 int(remaining_steps), _ptr(ids), _ptr(commit), _ptr(conf))
+    if err:
+        raise ValueError("oracle unmask_f64 failed with code %d" % err)
+    return ids, commit, conf
+
+
+def lmhead_unmask(hidden: np.ndarray, weight: np.ndarray, mask: np.ndarray,
+                  k_commit: Optional[np.ndarray] = None, remaining_steps: int = 1,
+                  seqs: Optional[Sequence[int]] = None, with_logits: bool = False):
+    """LM head then count-form unmask.  hidden [B*S, H] and weight [V, H] as
+    bf16 bits, mask [B, S].  ``seqs`` restricts the evaluation to those
+    sequences (the commit ranks within a sequence, so whole sequences are the
+    unit); results then have len(seqs) rows of S."""
+    mask = _c(mask, np.uint8)
+    B, S = mask.shape
+    if seqs is None:
+        seqs = list(range(B))
+    seqs = [int(b) for b in seqs]
+    rows = [b * S + t for b in seqs for t in range(S)]
+    logits = lmhead_logits(hidden, weight, rows)
+    kc = None if k_commit is None else np.asarray(k_commit, dtype=np.int32).reshape(B)[seqs]
+    res = unmask_f64(logits, mask[seqs], kc, remaining_steps)
+    return res + (logits,) if with_logits else res
 
 
 def unmask_threshold(logits: np.ndarray, mask: np.ndarray, gamma: float,

@@ -221,14 +221,10 @@ static void row_conf(const float *row, int V, int32_t *id, double *conf) {
  * ids/conf are written for every row; commit[b*S+t] = 1 exactly on the
  * committed positions.
  */
-int tto_unmask(int B, int S, int V, const float *logits, const uint8_t *mask,
-               const int32_t *k_commit, int remaining_steps, int32_t *ids,
-               uint8_t *commit, double *conf) {
-  if (B < 0 || S < 1 || V < 1) return TTO_ERR_ARG;
-  if (!k_commit && remaining_steps < 1) return TTO_ERR_ARG;
-#pragma omp parallel for schedule(static)
-  for (int r = 0; r < B * S; ++r) row_conf(logits + (size_t)r * V, V, ids + r, conf + r);
-
+/* Count-form commit over precomputed confidences (shared by the fp32-logits
+ * and the LM-head entry points below). */
+static int commit_count(int B, int S, const uint8_t *mask, const int32_t *k_commit,
+                        int remaining_steps, const double *conf, uint8_t *commit) {
   int *cand = (int *)malloc(sizeof(int) * (size_t)S);
   if (!cand) return TTO_ERR_MEM;
   for (int b = 0; b < B; ++b) {
@@ -257,6 +253,73 @@ int tto_unmask(int B, int S, int V, const float *logits, const uint8_t *mask,
   }
   free(cand);
   return TTO_OK;
+}
+
+int tto_unmask(int B, int S, int V, const float *logits, const uint8_t *mask,
+               const int32_t *k_commit, int remaining_steps, int32_t *ids,
+               uint8_t *commit, double *conf) {
+  if (B < 0 || S < 1 || V < 1) return TTO_ERR_ARG;
+  if (!k_commit && remaining_steps < 1) return TTO_ERR_ARG;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < B * S; ++r) row_conf(logits + (size_t)r * V, V, ids + r, conf + r);
+  return commit_count(B, S, mask, k_commit, remaining_steps, conf, commit);
+}
+
+/*
+ * LM head ahead of the unmask.
+ *
+ * [REVIEW, "Training and sampling"] and [SKY, "Generating Text in Parallel
+ * Like Solving a Sudoku"]: the denoiser predicts every masked position of the
+ * block, i.e. its final hidden state goes through the model's output head to
+ * logits over the vocabulary, and the confidence rule above runs on those
+ * logits.  The pages give neither the head's shape nor its weights; the head
+ * is read as a plain linear map without bias, logits[r][v] = sum_h
+ * hidden[r][h] * weight[v][h] (weight stored one vocabulary row after
+ * another), inputs in bf16, evaluated here exactly in fp64.
+ *
+ * rows (may be NULL = 0..nrows-1) selects which hidden rows to evaluate;
+ * logits receives nrows x V values.
+ */
+int tto_lmhead_logits(int R, int H, int V, const uint16_t *hidden, const uint16_t *weight,
+                      const int32_t *rows, int nrows, double *logits) {
+  if (R < 0 || H < 1 || V < 1 || nrows < 0) return TTO_ERR_ARG;
+  for (int i = 0; i < nrows; ++i) {
+    const int r = rows ? rows[i] : i;
+    if (r < 0 || r >= R) return TTO_ERR_ARG;
+  }
+#pragma omp parallel for schedule(static)
+  for (long iv = 0; iv < (long)nrows * V; ++iv) {
+    const int i = (int)(iv / V), v = (int)(iv % V);
+    const int r = rows ? rows[i] : i;
+    double acc = 0.0;
+    for (int h = 0; h < H; ++h)
+      acc += elem(hidden, (size_t)r * H + h, 1) * elem(weight, (size_t)v * H + h, 1);
+    logits[iv] = acc;
+  }
+  return TTO_OK;
+}
+
+/* The confidence of one row of fp64 logits (same definition as row_conf). */
+static void row_conf_f64(const double *row, int V, int32_t *id, double *conf) {
+  double m = -INFINITY;
+  int arg = 0;
+  for (int v = 0; v < V; ++v)
+    if (row[v] > m) { m = row[v]; arg = v; }
+  double Z = 0.0;
+  for (int v = 0; v < V; ++v) Z += exp(row[v] - m);
+  *id = arg;
+  *conf = 1.0 / Z;
+}
+
+/* Count-form unmask on fp64 logits (the LM head's exact output). */
+int tto_unmask_f64(int B, int S, int V, const double *logits, const uint8_t *mask,
+                   const int32_t *k_commit, int remaining_steps, int32_t *ids,
+                   uint8_t *commit, double *conf) {
+  if (B < 0 || S < 1 || V < 1) return TTO_ERR_ARG;
+  if (!k_commit && remaining_steps < 1) return TTO_ERR_ARG;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < B * S; ++r) row_conf_f64(logits + (size_t)r * V, V, ids + r, conf + r);
+  return commit_count(B, S, mask, k_commit, remaining_steps, conf, commit);
 }
 
 /*

@@ -42,6 +42,11 @@ MUTATIONS = [
     ("chunk_excludes_self", "const int Sk = causal ? t + 1 : S;", "const int Sk = causal ? t : S;"),
     ("chunk_not_causal", "const int Sk = causal ? t + 1 : S;", "const int Sk = S;"),
     ("chunk_anticausal", "const int Sk = causal ? t + 1 : S;", "const int Sk = causal ? S - t : S;"),
+    ("lmhead_weight_transposed", "elem(weight, (size_t)v * H + h, 1)", "elem(weight, (size_t)h * V + v, 1)"),
+    ("lmhead_drops_last_feature", "for (int h = 0; h < H; ++h)", "for (int h = 0; h < H - 1; ++h)"),
+    ("lmhead_rows_ignored", "const int r = rows ? rows[i] : i;", "const int r = i;"),
+    ("lmhead_argmax_last_on_tie", "if (row[v] > m) { m = row[v]; arg = v; }",
+     "if (row[v] >= m) { m = row[v]; arg = v; }"),
 ]
 
 
@@ -90,6 +95,8 @@ def _pins_pass():
             return False
         if not _chunk_pins_pass():
             return False
+        if not _lmhead_pins_pass():
+            return False
     except ValueError:
         return False
     return True
@@ -113,6 +120,19 @@ def _chunk_pins_pass():
     checks = [lambda case=case: C.test_hand_cases(case) for case in C.G["cases"]]
     checks += [lambda: C.test_against_masked_sdpa([21, 0, 40], 4, 8, 2, 16),
                C.test_future_chunk_tokens_do_not_matter]
+    for f in checks:
+        try:
+            f()
+        except AssertionError:
+            return False
+    return True
+
+
+def _lmhead_pins_pass():
+    import test_oracle_lmhead as M
+    checks = [M.test_hand_case, lambda: M.test_identity_head_is_unmask(0),
+              lambda: M.test_permuted_head(0), M.test_brute_force_tiny,
+              M.test_doubled_weight_doubles_logits, M.test_sequence_selection]
     for f in checks:
         try:
             f()
