@@ -223,6 +223,52 @@ int tt_unmask_threshold(const float *logits, uint8_t *mask, float gamma, int32_t
                         float *conf_out, int32_t *nsteps, uint32_t flags, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/*
+ * LM head fused with the confidence unmask.  The denoiser predicts every
+ * masked slot through the model's output head ("Training and sampling",
+ * paperfeed review; "Generating Text in Parallel Like Solving a Sudoku",
+ * kongchang explainer); the head is read as a bias-free linear map:
+ *
+ *   logits[r, v] = sum_h hidden[r, h] * weight[v, h]     (r = b*S + t)
+ *
+ * and the result is exactly tt_unmask (count form) on those logits, except
+ * that the logits are never written to memory: the head's matrix product
+ * (bf16 inputs, fp32 accumulation, on the matrix cores) reduces each tile of
+ * logits on the spot to the per-row maximum, its lowest index and the sum
+ * of exp(logit - max).  ids_out / commit_out / conf_out, mask, k_commit,
+ * remaining_steps and flags are as in tt_unmask.
+ *
+ *   hidden      bf16 [B*S, H], 16-byte aligned (the final hidden state)
+ *   weight      bf16 [V, H], 16-byte aligned (one vocabulary row after another)
+ *   batch, block, vocab  as in tt_unmask
+ *   hidden_size H: a multiple of 32 in [32, 65536]
+ *
+ * Differences from tt_unmask on the same logits come only from the fp32
+ * rounding of the logits (accumulation order): ids may differ where the two
+ * largest logits of a row are that close, commits where confidences are.
+ * Workspace: tt_lmhead_unmask_workspace_bytes (16-byte aligned, caller-owned,
+ * needed for batch > 0).  Errors as tt_unmask; TT_ERR_SHAPE for H.
+ */
+int tt_lmhead_unmask_workspace_bytes(int32_t batch, int32_t block, int32_t vocab,
+                                     int32_t hidden_size, size_t *bytes);
+int tt_lmhead_unmask(const void *hidden, const void *weight, uint8_t *mask,
+                     const int32_t *k_commit, int32_t remaining_steps, int32_t batch,
+                     int32_t block, int32_t vocab, int32_t hidden_size, int32_t *ids_out,
+                     uint8_t *commit_out, float *conf_out, uint32_t flags, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * The same fused head followed by the threshold form of the commit rule
+ * (tt_unmask_threshold's gamma, nsteps and rule); arguments as in
+ * tt_lmhead_unmask and tt_unmask_threshold, same workspace size as
+ * tt_lmhead_unmask.
+ */
+int tt_lmhead_unmask_threshold(const void *hidden, const void *weight, uint8_t *mask,
+                               float gamma, int32_t batch, int32_t block, int32_t vocab,
+                               int32_t hidden_size, int32_t *ids_out, uint8_t *commit_out,
+                               float *conf_out, int32_t *nsteps, uint32_t flags, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *tt_status_str(int status);
 

@@ -95,9 +95,10 @@ def assert_attn_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = 
     return max_abs, rel
 
 
-def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff):
+def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff, tie=COMMIT_TIE):
     """Commit comparator: exact count, only masked slots, and any difference
-    from the oracle's set only among near-ties of the k-th confidence."""
+    from the oracle's set only among near-ties (within ``tie``) of the k-th
+    confidence."""
     B, S = mask.shape
     for b in range(B):
         cg, cr = commit_gpu[b].astype(bool), commit_ref[b].astype(bool)
@@ -108,11 +109,11 @@ def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff):
         if diff.size:
             masked_conf = np.sort(conf_ref[b][m])[::-1]
             cstar = masked_conf[k_eff[b] - 1]
-            assert np.all(np.abs(conf_ref[b][diff] - cstar) <= COMMIT_TIE), \
+            assert np.all(np.abs(conf_ref[b][diff] - cstar) <= tie), \
                 (b, diff, conf_ref[b][diff], cstar)
 
 
-def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma):
+def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma, tie=COMMIT_TIE):
     """Threshold-rule comparator.  The GPU decides conf > gamma on its fp32
     confidence, the oracle's confidence is fp64, so a slot whose oracle
     confidence lies within COMMIT_TIE of gamma may go either way; the same band
@@ -129,8 +130,8 @@ def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma):
         if not m.any():
             assert not cg.any()
             continue
-        sure = m & (c > gamma + COMMIT_TIE)
-        near = m & (np.abs(c - gamma) <= COMMIT_TIE)
+        sure = m & (c > gamma + tie)
+        near = m & (np.abs(c - gamma) <= tie)
         if sure.any():
             assert np.all(cg[sure]), (b, "a slot surely above gamma was not committed")
             assert not np.any(cg & m & ~sure & ~near), (b, "a slot surely below gamma committed")
@@ -140,5 +141,5 @@ def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma):
         # commits one slot whose confidence is within the band of the maximum)
         assert cg.any(), (b, "no progress")
         judged_above = np.all(near[cg])
-        fallback = cg.sum() == 1 and abs(c[cg][0] - c[m].max()) <= COMMIT_TIE
+        fallback = cg.sum() == 1 and abs(c[cg][0] - c[m].max()) <= tie
         assert judged_above or fallback, (b, np.nonzero(cg)[0], c[cg], c[m].max())

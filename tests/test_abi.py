@@ -190,3 +190,49 @@ def test_unmask_threshold_nulls_and_workspace(lib):
     assert st == tt.load_library().tt_unmask(FAKE, FAKE, None, 1, 2, 16, 131072, FAKE, FAKE, None,
                                              0, FAKE, ctypes.c_size_t(16), None)
     assert st == -5
+
+
+LMHEAD_BAD = [
+    ("hidden31", dict(H=31), -2),
+    ("hidden0", dict(H=0), -2),
+    ("hidden_too_big", dict(H=65536 + 32), -2),
+    ("block0", dict(S=0), -2),
+    ("vocab0", dict(V=0), -2),
+    ("remaining0", dict(rem=0, k=None), -2),
+    ("flags", dict(flags=2), -4),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", LMHEAD_BAD, ids=[u[0] for u in LMHEAD_BAD])
+def test_lmhead_validation(lib, name, kw, code):
+    a = dict(B=2, S=16, V=1000, H=256, rem=1, k=FAKE, flags=0)
+    a.update(kw)
+    st = lib.tt_lmhead_unmask(FAKE, FAKE, FAKE, a["k"], a["rem"], a["B"], a["S"], a["V"], a["H"],
+                              FAKE, FAKE, None, a["flags"], FAKE, ctypes.c_size_t(1 << 30), None)
+    assert st == code
+    if name != "remaining0":
+        st = lib.tt_lmhead_unmask_threshold(FAKE, FAKE, FAKE, 0.8, a["B"], a["S"], a["V"], a["H"],
+                                            FAKE, FAKE, None, None, a["flags"], FAKE,
+                                            ctypes.c_size_t(1 << 30), None)
+        assert st == code
+
+
+def test_lmhead_nulls_alignment_workspace(lib):
+    args = lambda hid, w, ws, n: (hid, w, FAKE, None, 1, 2, 16, 1000, 256, FAKE, FAKE, None, 0, ws,
+                                  ctypes.c_size_t(n), None)
+    assert lib.tt_lmhead_unmask(*args(None, FAKE, FAKE, 1 << 30)) == -1
+    assert lib.tt_lmhead_unmask(*args(FAKE, None, FAKE, 1 << 30)) == -1
+    odd = ctypes.c_void_p((1 << 20) + 8)  # 8-byte aligned only
+    assert lib.tt_lmhead_unmask(*args(odd, FAKE, FAKE, 1 << 30)) == -4
+    assert lib.tt_lmhead_unmask(*args(FAKE, odd, FAKE, 1 << 30)) == -4
+    need = ctypes.c_size_t(0)
+    assert lib.tt_lmhead_unmask_workspace_bytes(2, 16, 1000, 256, ctypes.byref(need)) == 0
+    # per (row, 128-entry chunk) partials plus one merged partial per row, 16 bytes each
+    assert need.value >= 32 * (8 + 1) * 16
+    assert lib.tt_lmhead_unmask(*args(FAKE, FAKE, FAKE, need.value - 1)) == -5
+    assert lib.tt_lmhead_unmask(*args(FAKE, FAKE, None, 1 << 30)) == -5
+    zero = ctypes.c_size_t(7)
+    assert lib.tt_lmhead_unmask_workspace_bytes(0, 16, 1000, 256, ctypes.byref(zero)) == 0
+    assert zero.value == 0
+    assert lib.tt_lmhead_unmask(FAKE, FAKE, FAKE, None, 1, 0, 16, 1000, 256, FAKE, FAKE, None, 0,
+                                None, ctypes.c_size_t(0), None) == 0

@@ -24,7 +24,9 @@ TT_F32 = 1
 TT_UNMASK_UPDATE_MASK = 1
 
 EXPORTS = ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_chunk_attn", "tt_kv_append",
-           "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold", "tt_status_str",
+           "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold",
+           "tt_lmhead_unmask_workspace_bytes", "tt_lmhead_unmask", "tt_lmhead_unmask_threshold",
+           "tt_status_str",
            "tt_last_error", "tt_abi_version")
 
 
@@ -69,13 +71,20 @@ def load_library(path: Optional[str] = None):
     lib.tt_unmask.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, ctypes.c_uint32, P, SZ, P]
     lib.tt_unmask_threshold.argtypes = [P, P, ctypes.c_float, I32, I32, I32, P, P, P, P,
                                         ctypes.c_uint32, P, SZ, P]
+    lib.tt_lmhead_unmask_workspace_bytes.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
+    lib.tt_lmhead_unmask.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, P, P,
+                                     ctypes.c_uint32, P, SZ, P]
+    lib.tt_lmhead_unmask_threshold.argtypes = [P, P, P, ctypes.c_float, I32, I32, I32, I32, P, P,
+                                               P, P, ctypes.c_uint32, P, SZ, P]
     lib.tt_status_str.argtypes = [ctypes.c_int]
     lib.tt_status_str.restype = ctypes.c_char_p
     lib.tt_last_error.argtypes = []
     lib.tt_last_error.restype = ctypes.c_char_p
     lib.tt_abi_version.argtypes = []
     for name in ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_kv_append",
-                 "tt_unmask_workspace_bytes", "tt_unmask", "tt_abi_version"):
+                 "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold",
+                 "tt_lmhead_unmask_workspace_bytes", "tt_lmhead_unmask",
+                 "tt_lmhead_unmask_threshold", "tt_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
@@ -222,6 +231,48 @@ def tt_unmask_threshold(logits, mask, gamma: float, ids_out, commit_out, conf_ou
     _check(load_library().tt_unmask_threshold(
         _ptr(logits, "logits", torch.float32, B * S * V), _ptr(mask, "mask", torch.uint8, B * S),
         float(gamma), B, S, V, _ptr(ids_out, "ids_out", torch.int32, B * S),
+        _ptr(commit_out, "commit_out", torch.uint8, B * S),
+        _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True),
+        _ptr(nsteps, "nsteps", torch.int32, B, allow_none=True), int(flags),
+        _ptr(workspace, "workspace", allow_none=True), nbytes, _stream(stream)))
+
+
+def tt_lmhead_unmask_workspace_bytes(batch: int, block: int, vocab: int, hidden: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().tt_lmhead_unmask_workspace_bytes(batch, block, vocab, hidden,
+                                                           ctypes.byref(n)))
+    return n.value
+
+
+def tt_lmhead_unmask(hidden, weight, mask, k_commit, remaining_steps: int, ids_out, commit_out,
+                     conf_out=None, flags: int = 0, workspace=None, stream=None) -> None:
+    """LM head fused with the count-form unmask (see include/tt.h)."""
+    torch = _torch()
+    B, S = mask.shape
+    V, H = weight.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().tt_lmhead_unmask(
+        _ptr(hidden, "hidden", torch.bfloat16, B * S * H), _ptr(weight, "weight", torch.bfloat16, V * H),
+        _ptr(mask, "mask", torch.uint8, B * S),
+        _ptr(k_commit, "k_commit", torch.int32, B, allow_none=True), int(remaining_steps),
+        B, S, V, H, _ptr(ids_out, "ids_out", torch.int32, B * S),
+        _ptr(commit_out, "commit_out", torch.uint8, B * S),
+        _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True), int(flags),
+        _ptr(workspace, "workspace", allow_none=True), nbytes, _stream(stream)))
+
+
+def tt_lmhead_unmask_threshold(hidden, weight, mask, gamma: float, ids_out, commit_out,
+                               conf_out=None, nsteps=None, flags: int = 0, workspace=None,
+                               stream=None) -> None:
+    """LM head fused with the threshold-form unmask (see include/tt.h)."""
+    torch = _torch()
+    B, S = mask.shape
+    V, H = weight.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().tt_lmhead_unmask_threshold(
+        _ptr(hidden, "hidden", torch.bfloat16, B * S * H), _ptr(weight, "weight", torch.bfloat16, V * H),
+        _ptr(mask, "mask", torch.uint8, B * S), float(gamma), B, S, V, H,
+        _ptr(ids_out, "ids_out", torch.int32, B * S),
         _ptr(commit_out, "commit_out", torch.uint8, B * S),
         _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True),
         _ptr(nsteps, "nsteps", torch.int32, B, allow_none=True), int(flags),

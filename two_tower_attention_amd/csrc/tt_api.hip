@@ -270,4 +270,103 @@ int tt_unmask_threshold(const float *logits, uint8_t *mask, float gamma, int32_t
   return ok();
 }
 
+// ---- LM head fused with the unmask ------------------------------------
+
+static int check_lmhead_shape(int32_t B, int32_t S, int32_t V, int32_t H) {
+  const int st = check_unmask_shape(B, S, V);
+  if (st) return st;
+  if (H < 32 || H > 65536 || H % 32 != 0)
+    return fail(TT_ERR_SHAPE, "hidden size %d must be a multiple of 32 in [32, 65536]", H);
+  return TT_OK;
+}
+
+static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// parts [R, chunks] then the merged row partials [R]
+static size_t lmhead_ws_bytes(int32_t B, int32_t S, int32_t V) {
+  const size_t R = (size_t)B * S;
+  return round256(R * tt::lmhead_chunks(V) * sizeof(tt::UnmaskPart)) +
+         round256(R * sizeof(tt::UnmaskPart));
+}
+
+int tt_lmhead_unmask_workspace_bytes(int32_t B, int32_t S, int32_t V, int32_t H, size_t *bytes) {
+  if (!bytes) return fail(TT_ERR_NULL, "bytes is NULL");
+  const int st = check_lmhead_shape(B, S, V, H);
+  if (st) return st;
+  *bytes = B == 0 ? 0 : lmhead_ws_bytes(B, S, V);
+  return ok();
+}
+
+// Validation and the fused head + row reduction shared by the two commit forms;
+// on success *merged points at the [B*S] row partials in the workspace.
+static int lmhead_rows(const void *hidden, const void *weight, int32_t B, int32_t S, int32_t V,
+                       int32_t H, void *workspace, size_t workspace_bytes, hipStream_t s,
+                       tt::UnmaskPart **merged) {
+  if (!hidden || !weight) return fail(TT_ERR_NULL, "hidden and weight are required");
+  if (!aligned(hidden, 16) || !aligned(weight, 16))
+    return fail(TT_ERR_UNSUPPORTED, "hidden and weight must be 16-byte aligned");
+  const size_t need = lmhead_ws_bytes(B, S, V);
+  if (!workspace || workspace_bytes < need)
+    return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(TT_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (device_cus(nullptr) <= 0) return fail(TT_ERR_NO_DEVICE, "no HIP device");
+  const int R = B * S;
+  tt::UnmaskPart *parts = (tt::UnmaskPart *)workspace;
+  *merged = (tt::UnmaskPart *)((unsigned char *)workspace +
+                               round256((size_t)R * tt::lmhead_chunks(V) * sizeof(tt::UnmaskPart)));
+  hipError_t e = tt::launch_lmhead_parts(hidden, weight, R, H, V, parts, s);
+  if (e == hipSuccess) e = tt::launch_unmask_merge(parts, tt::lmhead_chunks(V), R, *merged, s);
+  if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return TT_OK;
+}
+
+int tt_lmhead_unmask(const void *hidden, const void *weight, uint8_t *mask,
+                     const int32_t *k_commit, int32_t remaining_steps, int32_t B, int32_t S,
+                     int32_t V, int32_t H, int32_t *ids_out, uint8_t *commit_out, float *conf_out,
+                     uint32_t flags, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_lmhead_shape(B, S, V, H);
+  if (st) return st;
+  if (flags & ~TT_UNMASK_UPDATE_MASK) return fail(TT_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (!k_commit && remaining_steps < 1)
+    return fail(TT_ERR_SHAPE, "remaining_steps %d < 1 with k_commit NULL", remaining_steps);
+  if (B == 0) return ok();
+  if (!mask || !ids_out || !commit_out)
+    return fail(TT_ERR_NULL, "mask, ids_out and commit_out are required");
+  if (!aligned(ids_out, 4) || (k_commit && !aligned(k_commit, 4)) || (conf_out && !aligned(conf_out, 4)))
+    return fail(TT_ERR_UNSUPPORTED, "ids_out, k_commit, conf_out must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  tt::UnmaskPart *merged = nullptr;
+  st = lmhead_rows(hidden, weight, B, S, V, H, workspace, workspace_bytes, s, &merged);
+  if (st) return st;
+  const hipError_t e = tt::launch_unmask_commit(merged, 1, B, S, mask, k_commit, remaining_steps,
+                                                ids_out, commit_out, conf_out, flags, s);
+  if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int tt_lmhead_unmask_threshold(const void *hidden, const void *weight, uint8_t *mask, float gamma,
+                               int32_t B, int32_t S, int32_t V, int32_t H, int32_t *ids_out,
+                               uint8_t *commit_out, float *conf_out, int32_t *nsteps,
+                               uint32_t flags, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  int st = check_lmhead_shape(B, S, V, H);
+  if (st) return st;
+  if (flags & ~TT_UNMASK_UPDATE_MASK) return fail(TT_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (!std::isfinite(gamma)) return fail(TT_ERR_SHAPE, "gamma must be finite");
+  if (B == 0) return ok();
+  if (!mask || !ids_out || !commit_out)
+    return fail(TT_ERR_NULL, "mask, ids_out and commit_out are required");
+  if (!aligned(ids_out, 4) || (nsteps && !aligned(nsteps, 4)) || (conf_out && !aligned(conf_out, 4)))
+    return fail(TT_ERR_UNSUPPORTED, "ids_out, nsteps, conf_out must be 4-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  tt::UnmaskPart *merged = nullptr;
+  st = lmhead_rows(hidden, weight, B, S, V, H, workspace, workspace_bytes, s, &merged);
+  if (st) return st;
+  const hipError_t e = tt::launch_unmask_threshold_commit(merged, 1, B, S, mask, gamma, ids_out,
+                                                          commit_out, conf_out, nsteps, flags, s);
+  if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

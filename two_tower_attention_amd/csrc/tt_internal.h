@@ -45,6 +45,16 @@ hipError_t launch_kv_append(const tt_attn_desc &d, const void *k_blk, const void
                             void *k_pages, void *v_pages, const int32_t *page_table,
                             int32_t *ctx_lens, hipStream_t stream);
 
+// Per (row, vocabulary chunk) partial of the unmask's row reduction:
+// m = max, s = sum exp(l - m), idx = lowest index attaining m.  A chunk with
+// no element has m = -inf, s = 0, idx = INT_MAX.
+struct UnmaskPart {
+  float m;
+  float s;
+  int idx;
+  int pad;
+};
+
 struct UnmaskPlan {
   int B, S, V;
   int chunks;       // vocabulary chunks per row
@@ -63,5 +73,25 @@ hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uin
                                    float gamma, int32_t *ids, uint8_t *commit, float *conf,
                                    int32_t *nsteps, uint32_t flags, void *workspace,
                                    hipStream_t stream);
+
+// Merges `chunks` partials per row of parts [rows, chunks] into out [rows].
+hipError_t launch_unmask_merge(const UnmaskPart *parts, int chunks, int rows, UnmaskPart *out,
+                               hipStream_t stream);
+
+// The commit stage of tt_unmask / tt_unmask_threshold on row partials
+// [B*S, chunks].
+hipError_t launch_unmask_commit(const UnmaskPart *parts, int chunks, int B, int S, uint8_t *mask,
+                                const int32_t *k_commit, int remaining_steps, int32_t *ids,
+                                uint8_t *commit, float *conf, uint32_t flags, hipStream_t stream);
+hipError_t launch_unmask_threshold_commit(const UnmaskPart *parts, int chunks, int B, int S,
+                                          uint8_t *mask, float gamma, int32_t *ids,
+                                          uint8_t *commit, float *conf, int32_t *nsteps,
+                                          uint32_t flags, hipStream_t stream);
+
+// LM head fused with the unmask's row reduction: hidden [R, H] and weight
+// [V, H] in bf16 -> per (row, 128-vocabulary chunk) partials [R, lmhead_chunks(V)].
+int lmhead_chunks(int V);
+hipError_t launch_lmhead_parts(const void *hidden, const void *weight, int R, int H, int V,
+                               UnmaskPart *parts, hipStream_t stream);
 
 }  // namespace tt

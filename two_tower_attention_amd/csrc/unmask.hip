@@ -23,12 +23,7 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct Part {
-  float m;   // max
-  float s;   // sum exp(l - m)
-  int idx;   // lowest index attaining m
-  int pad;
-};
+typedef UnmaskPart Part;
 
 // exp(x - m) for x <= m; m == -inf only when every x seen is -inf (-> 0).
 __device__ __forceinline__ float ex(float x, float m) {
@@ -207,7 +202,56 @@ __global__ __launch_bounds__(64) void unmask_threshold_commit_kernel(
   if (t == 0 && nsteps && n > 0) nsteps[b] += 1;
 }
 
+// One wave per row: lane j merges chunks j, j + 64, ...; then a wave
+// reduction.  The merge keeps the lower index on equal maxima, so the order
+// of chunks does not matter.
+__global__ __launch_bounds__(64) void unmask_merge_kernel(const Part *parts, int chunks,
+                                                          Part *out) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  Acc a;
+  a.init();
+  for (int c = lane; c < chunks; c += 64) {
+    const Part pt = parts[(size_t)r * chunks + c];
+    a.merge(pt.m, pt.s, pt.idx);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(a.m, o, 64);
+    const float s2 = __shfl_xor(a.s, o, 64);
+    const int i2 = __shfl_xor(a.idx, o, 64);
+    a.merge(m2, s2, i2);
+  }
+  if (lane == 0) {
+    Part pt;
+    pt.m = a.m; pt.s = a.s; pt.idx = a.idx; pt.pad = 0;
+    out[r] = pt;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_unmask_merge(const UnmaskPart *parts, int chunks, int rows, UnmaskPart *out,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(unmask_merge_kernel, dim3(rows), dim3(64), 0, stream, parts, chunks, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask_commit(const UnmaskPart *parts, int chunks, int B, int S, uint8_t *mask,
+                                const int32_t *k_commit, int remaining_steps, int32_t *ids,
+                                uint8_t *commit, float *conf, uint32_t flags, hipStream_t stream) {
+  hipLaunchKernelGGL(unmask_commit_kernel, dim3(B), dim3(64), 0, stream, parts, chunks, S, mask,
+                     k_commit, remaining_steps, ids, commit, conf, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_unmask_threshold_commit(const UnmaskPart *parts, int chunks, int B, int S,
+                                          uint8_t *mask, float gamma, int32_t *ids,
+                                          uint8_t *commit, float *conf, int32_t *nsteps,
+                                          uint32_t flags, hipStream_t stream) {
+  hipLaunchKernelGGL(unmask_threshold_commit_kernel, dim3(B), dim3(64), 0, stream, parts, chunks,
+                     S, mask, gamma, ids, commit, conf, nsteps, flags);
+  return hipGetLastError();
+}
 
 UnmaskPlan plan_unmask(int B, int S, int V) {
   UnmaskPlan p{};
@@ -241,9 +285,8 @@ hipError_t launch_unmask(const UnmaskPlan &p, const float *logits, uint8_t *mask
   Part *parts = (Part *)workspace;
   hipError_t e = launch_rowreduce(p, logits, parts, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(unmask_commit_kernel, dim3(p.B), dim3(64), 0, stream, parts, p.chunks, p.S,
-                     mask, k_commit, remaining_steps, ids, commit, conf, flags);
-  return hipGetLastError();
+  return launch_unmask_commit(parts, p.chunks, p.B, p.S, mask, k_commit, remaining_steps, ids,
+                              commit, conf, flags, stream);
 }
 
 hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uint8_t *mask,
@@ -253,9 +296,8 @@ hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uin
   Part *parts = (Part *)workspace;
   hipError_t e = launch_rowreduce(p, logits, parts, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(unmask_threshold_commit_kernel, dim3(p.B), dim3(64), 0, stream, parts,
-                     p.chunks, p.S, mask, gamma, ids, commit, conf, nsteps, flags);
-  return hipGetLastError();
+  return launch_unmask_threshold_commit(parts, p.chunks, p.B, p.S, mask, gamma, ids, commit, conf,
+                                        nsteps, flags, stream);
 }
 
 }  // namespace tt

@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "AttnCase", "make_attn_case", "bf16_bits", "bits_to_f32",
     "config1", "config2", "config3", "config4", "config5",
-    "Loop", "make_logits", "NAN_BF16",
+    "Loop", "make_logits", "NAN_BF16", "LmHeadCase", "make_lmhead_case",
 ]
 
 NAN_BF16 = np.uint16(0x7FC0)
@@ -276,3 +276,41 @@ def peaked_logits(rng: np.random.Generator, blk: PeakedBlock, step: int,
     height = np.log(blk.vocab) + 0.5 * sigma * sigma + margin
     x[np.arange(rows), blk.spike_ids] = height.astype(np.float32)
     return x
+
+
+# ---------------------------------------------------------------------------
+# LM head ahead of the unmask.  The pages give no head shape; the hidden size
+# is H_q * D of the attention configs (4096) and the vocabulary that of the
+# unmask workload (131072).  Weights are scaled so that the logits are
+# ~ N(0, sigma^2), the distribution of the unmask workload's logits.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LmHeadCase:
+    B: int
+    S: int
+    H: int
+    V: int
+    hidden: np.ndarray   # uint16 bf16 bits [B*S, H]
+    weight: np.ndarray   # uint16 bf16 bits [V, H]
+    seed: int
+
+
+def make_lmhead_case(rng: np.random.Generator, B: int, S: int, H: int, V: int,
+                     sigma: float = 3.0, row_scale: Optional[np.ndarray] = None,
+                     seed: int = 0) -> LmHeadCase:
+    """Hidden state ~ N(0, 1) (times ``row_scale[r]`` per row when given: larger
+    scales give more confident rows) and head weights ~ N(0, sigma^2 / H),
+    drawn hidden first, then the weight in blocks of vocabulary rows."""
+    hidden = rng.standard_normal((B * S, H), dtype=np.float32)
+    if row_scale is not None:
+        hidden *= np.asarray(row_scale, dtype=np.float32).reshape(-1, 1)
+    hidden_bits = bf16_bits(hidden)
+    weight = np.empty((V, H), dtype=np.uint16)
+    step = max(1, (1 << 24) // H)
+    for v0 in range(0, V, step):
+        n = min(step, V - v0)
+        w = rng.standard_normal((n, H), dtype=np.float32)
+        w *= np.float32(sigma / math.sqrt(H))
+        weight[v0:v0 + n] = bf16_bits(w)
+    return LmHeadCase(B=B, S=S, H=H, V=V, hidden=hidden_bits, weight=weight, seed=seed)
