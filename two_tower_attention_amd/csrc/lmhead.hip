@@ -20,13 +20,15 @@
 // epilogue's row reductions are lane-local plus one lane-pair exchange.
 //
 // Operands stream HBM -> LDS by direct loads through buffer descriptors into
-// a ring of kSlots stages; a stage is 32 reduction elements (64 bytes) of the
-// tile's 256 weight rows and 256 hidden rows.  Inside a stage each 64-byte
-// row keeps its four 16-byte chunks XOR-swizzled by bits 2..3 of the row
-// index, which keeps the operand reads (32 consecutive rows, one chunk)
-// free of bank conflicts; each direct load fills 1 KiB = 16 rows, and a lane
-// fetches whichever chunk the swizzle puts at its slot.  One per-lane offset
-// serves every load: load n of a tile adds n * 16 rows as a scalar offset.
+// a ring of kSlots stages; a stage is kKS reduction elements of the tile's
+// 256 weight rows and 256 hidden rows.  Small stages in many slots keep the
+// loads issued well ahead of their use (the ring's lead time is (kSlots - 2)
+// stages).  Inside a stage each row keeps its 16-byte chunks XOR-swizzled by
+// the row's position in its 256-byte group, which keeps the operand reads
+// (32 consecutive rows, one chunk) free of bank conflicts; each direct load
+// fills 1 KiB of rows, and a lane fetches whichever chunk the swizzle puts at
+// its slot.  One per-lane offset serves every load: load n of a tile adds its
+// first row as a scalar offset.
 #include <limits.h>
 
 #include "tt_internal.h"
@@ -37,15 +39,32 @@ namespace {
 constexpr int kVT = 256;                        // vocabulary rows per work-group tile
 constexpr int kRT = 256;                        // hidden rows per work-group tile
 constexpr int kChunk = 128;                     // vocabulary entries per partial
-constexpr int kKS = 32;                         // reduction elements per stage
-constexpr int kSlots = 4;                       // ring stages (kSlots - 1 in flight)
+#ifndef TT_LM_KS
+#define TT_LM_KS 32
+#endif
+#ifndef TT_LM_SLOTS
+#define TT_LM_SLOTS 4
+#endif
+constexpr int kKS = TT_LM_KS;                   // reduction elements per stage
+constexpr int kSlots = TT_LM_SLOTS;             // ring stages
 constexpr int kThreads = 256;                   // 4 waves
-constexpr int kRowBytes = kKS * 2;              // 64 bytes of one row per stage
-constexpr int kTileBytes = kVT * kRowBytes;     // 16 KiB: one operand's part of a stage
+constexpr int kNCh = kKS / 8;                   // 16-byte chunks per row per stage
+constexpr int kSteps = kKS / 16;                // MFMA reduction steps per stage
+constexpr int kRowBytes = kKS * 2;              // bytes of one row per stage
+constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one 1 KiB direct load fills
+constexpr int kSwz = 16 / kNCh;                 // rows per 256 bytes: the swizzle's row period
+constexpr int kTileBytes = kVT * kRowBytes;     // one operand's part of a stage
 constexpr int kStageBytes = 2 * kTileBytes;     // weight part, then hidden part
-constexpr int kLoads = kTileBytes / 1024 / 4;   // 4 KiB-loads per wave per operand per stage
+constexpr int kLoads = kTileBytes / 1024 / 4;   // 1 KiB loads per wave per operand per stage
 static_assert(kVT == kRT, "both operand parts of a stage have the same shape");
+static_assert(kKS == 16 || kKS == 32, "stage depth");
 static_assert(kLoads * 4 * 1024 == kTileBytes, "the waves share a stage's loads evenly");
+static_assert(kSlots >= 3 && (kSlots - 3) * 2 * kLoads < 64, "ring depth");
+static_assert(kSlots * kStageBytes <= 160 * 1024, "ring fits the LDS");
+
+// Physical 16-byte slot of logical chunk c in row r: XOR with the row's
+// position in its 256-byte group, so 16 consecutive rows cover all banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r / kSwz) % kNCh); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -64,10 +83,10 @@ struct Ops {
   bf16x8 w[4], x[4];
 };
 
-// Reads the wave's operands of reduction step ks (0, 1) of a stage.  Row r
-// of a part, logical chunk c sits at r * 64 + 16 * (c ^ ((r >> 2) & 3)); the
-// wave's rows are 32*b + ln of its 128-row half, so the XOR term depends on
-// ln only and the block offset goes into the instruction's immediate.
+// Reads the wave's operands of one reduction step of a stage.  Row r of a
+// part keeps logical chunk c at r * kRowBytes + 16 * swz(r, c); the wave's
+// rows are 32*b + ln of its 128-row half, so the swizzle depends on ln only
+// and the block offset goes into the instruction's immediate.
 __device__ __forceinline__ void read_ops(const unsigned char *stage, unsigned lane_off, int vw,
                                          int rw, Ops &o) {
 #pragma unroll
@@ -77,12 +96,11 @@ __device__ __forceinline__ void read_ops(const unsigned char *stage, unsigned la
   }
 }
 
-__device__ __forceinline__ void mfma_ops(const Ops &o, f32x16 (&acc)[4][4]) {
+// The four MFMAs of weight block vb (128 cycles of matrix-core work).
+__device__ __forceinline__ void mfma_row(const Ops &o, int vb, f32x16 (&acc)[4][4]) {
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[vb], o.x[rb], acc[vb][rb], 0, 0, 0);
+  for (int rb = 0; rb < 4; ++rb)
+    acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[vb], o.x[rb], acc[vb][rb], 0, 0, 0);
 }
 
 // lgkmcnt(0) only (gfx9 encoding): completes this wave's LDS reads.
@@ -94,6 +112,19 @@ template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+// Wait until at most `stages` stages of this wave's direct loads are in flight.
+template <int PER, int MAX>
+__device__ __forceinline__ void wait_stages(int stages) {
+  if constexpr (MAX > 0) {
+    if (stages >= MAX) {
+      vm_wait<PER * MAX>();
+      return;
+    }
+    wait_stages<PER, MAX - 1>(stages);
+  } else {
+    vm_wait<0>();
+  }
 }
 // Work-group barrier ordering LDS only (no global fence, which would drain
 // the direct loads still in flight).
@@ -110,8 +141,24 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 31, hl = lane >> 5;
   const int vw = wave >> 1, rw = wave & 1;
+  // Tile order.  Work-groups are dealt to the 8 XCDs round-robin (id % 8),
+  // and each XCD has its own L2.  The row tiles of one vocabulary tile read
+  // the same weight rows, so they go to ids 8 apart: same XCD, dispatched
+  // together, and the weight tile leaves HBM once.  (Vocabulary tiles past the
+  // last multiple of 8 use plain order.)
   const int nrt = (p.R + kRT - 1) / kRT;
-  const int rt = blockIdx.x % nrt, vt = blockIdx.x / nrt;  // the row tiles of a vocabulary tile run together
+  const int nvt = (p.V + kVT - 1) / kVT;
+  const int full = (nvt / 8) * 8 * nrt;
+  int rt, vt;
+  if ((int)blockIdx.x < full) {
+    const int q = blockIdx.x / (8 * nrt), rem = blockIdx.x % (8 * nrt);
+    rt = rem / 8;
+    vt = 8 * q + rem % 8;
+  } else {
+    const int j = blockIdx.x - full;
+    rt = j % nrt;
+    vt = (nvt / 8) * 8 + j / nrt;
+  }
   const int r0 = rt * kRT, v0 = vt * kVT;
   const int w_rows = min(kVT, p.V - v0), x_rows = min(kRT, p.R - r0);
   const __bf16 *wb = p.w + (size_t)v0 * p.H;
@@ -119,34 +166,41 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
   const int nst = p.H / kKS;
 
   // Direct loads: lane l of a load fills bytes 16l.. of 1 KiB = tile rows
-  // 16n + l/4 (n = the load), physical chunk l%4, i.e. logical chunk
-  // (l%4) ^ ((l/16)%4); rows past the operand's end read as zero (descriptor
-  // range).
-  const unsigned voff = (unsigned)(((lane >> 2) * p.H + 8 * ((lane & 3) ^ ((lane >> 4) & 3))) * 2);
-  auto issue = [&](int s) {
-    if (s >= nst) return;
+  // kRowsPerLoad*n + l/kNCh (n = the load), physical chunk l%kNCh, i.e. the
+  // logical chunk that swz() puts there; rows past the operand's end read as
+  // zero (descriptor range).  Load n adds n*kRowsPerLoad rows as a scalar
+  // offset, which leaves the swizzle unchanged (kRowsPerLoad is a multiple of
+  // its row period times kNCh).
+  static_assert(kRowsPerLoad % (kSwz * kNCh) == 0, "load boundaries keep the swizzle");
+  const int lrow = lane / kNCh;
+  const unsigned voff = (unsigned)((lrow * p.H + 8 * swz(lrow, lane % kNCh)) * 2);
+  // Load j (0 .. 2*kLoads-1) of this wave for stage s: weight part first.
+  // Issued one at a time between MFMA groups: the wave is the only one on
+  // its SIMD, and a load that waits for room in the memory queue holds up
+  // its instruction stream, so each load sits behind 128 cycles of queued
+  // matrix-core work instead of in a burst.
+  auto issue_one = [&](int s, int j) {
     unsigned char *st = ring + (s % kSlots) * kStageBytes;
     const int k0 = s * kKS;
-    const __amdgpu_buffer_rsrc_t rw_ = buffer_rsrc(wb + k0, (w_rows * p.H - k0) * 2);
-    const __amdgpu_buffer_rsrc_t rx_ = buffer_rsrc(xb + k0, (x_rows * p.H - k0) * 2);
+    const bool wpart = j < kLoads;
+    const int n = kLoads * wave + (wpart ? j : j - kLoads);
+    const __amdgpu_buffer_rsrc_t r =
+        wpart ? buffer_rsrc(wb + k0, (w_rows * p.H - k0) * 2) : buffer_rsrc(xb + k0, (x_rows * p.H - k0) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(st + (wpart ? 0 : kTileBytes) + n * 1024), 16,
+                                             voff, (unsigned)(n * kRowsPerLoad * p.H * 2), 0, 0);
+  };
+  auto issue = [&](int s) {
+    if (s >= nst) return;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int n = kLoads * wave + j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void *)(st + n * 1024), 16, voff,
-                                               (unsigned)(n * 32 * p.H), 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int n = kLoads * wave + j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx_, (lds_void *)(st + kTileBytes + n * 1024), 16,
-                                               voff, (unsigned)(n * 32 * p.H), 0, 0);
-    }
+    for (int j = 0; j < 2 * kLoads; ++j) issue_one(s, j);
   };
   constexpr int kPer = 2 * kLoads;  // direct loads per wave per stage
 
-  const int xo = (ln >> 2) & 3;
-  const unsigned off0 = (unsigned)(ln * kRowBytes + 16 * ((0 + hl) ^ xo));  // step 0: chunks 0, 1
-  const unsigned off1 = (unsigned)(ln * kRowBytes + 16 * ((2 + hl) ^ xo));  // step 1: chunks 2, 3
+  // operand read offsets of this lane for reduction step t of a stage:
+  // row ln of a 32-row block, logical chunk 2*t + hl
+  unsigned loff[kSteps];
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) loff[t] = (unsigned)(ln * kRowBytes + 16 * swz(ln, 2 * t + hl));
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -154,37 +208,49 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) acc[vb][rb] = f32x16{};
 
-  // prologue: stages 0 .. kSlots-2 in flight, stage 0 landed and visible
+  // Prologue: stages 0 .. kSlots-2 in flight, stage 0 landed and visible.
+  // In iteration s, stage s + 1 is awaited (it was issued kSlots - 3
+  // iterations earlier), so the operands of its first step can be read
+  // under the last MFMAs of stage s; stage s + kSlots - 1 then takes the
+  // slot of stage s - 1, which every wave has finished reading.
   for (int s = 0; s < kSlots - 1; ++s) issue(s);
-  if (nst >= 3) vm_wait<2 * kPer>();
-  else if (nst == 2) vm_wait<kPer>();
-  else vm_wait<0>();
+  wait_stages<kPer, kSlots - 2>(min(kSlots - 2, nst - 1));
   lds_barrier();
   Ops buf[2];
-  read_ops(ring, off0, vw, rw, buf[0]);
+  read_ops(ring, loff[0], vw, rw, buf[0]);
 
-  for (int s = 0; s < nst; ++s) {
-    // Stage s + 1 landed and visible to all waves; every wave is past stage
-    // s - 1, whose slot takes stage s + kSlots - 1.
+  // One stage: operands of its first step are in `cur`; the next stage's
+  // first operands end up in `cur` (two steps per stage) or `nxt` (one).
+  static_assert(2 * kLoads == 4 * kSteps, "one load per MFMA group");
+  auto stage = [&](int s, Ops &cur, Ops &nxt) {
     if (s + 1 < nst) {
-      if (s + 2 < nst) vm_wait<kPer>();
-      else vm_wait<0>();
+      wait_stages<kPer, kSlots - 3>(min(kSlots - 3, nst - 2 - s));
       lds_barrier();
     }
-    issue(s + kSlots - 1);
+    const int sn = s + kSlots - 1;  // stage loaded into the slot of stage s - 1
+    const bool load = sn < nst;
     const unsigned char *st = ring + (s % kSlots) * kStageBytes;
-    lds_wait();
-    __builtin_amdgcn_sched_barrier(0);
-    read_ops(st, off1, vw, rw, buf[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_ops(buf[0], acc);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_wait();
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < nst) read_ops(ring + ((s + 1) % kSlots) * kStageBytes, off0, vw, rw, buf[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_ops(buf[1], acc);
-    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char *st1 = ring + ((s + 1) % kSlots) * kStageBytes;
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      const Ops &o = t == 0 ? cur : nxt;
+      lds_wait();
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < kSteps) read_ops(st, loff[t + 1], vw, rw, nxt);
+      else if (s + 1 < nst) read_ops(st1, loff[0], vw, rw, kSteps == 2 ? cur : nxt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        mfma_row(o, vb, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (load) issue_one(sn, 4 * t + vb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  for (int s = 0; s < nst; ++s) {
+    stage(s, buf[0], buf[1]);
+    if (kSteps == 1) buf[0] = buf[1];  // register moves, under the MFMAs
   }
 
   // Epilogue.  Accumulator register q of lane (hl, ln) in block (vb, rb)
