@@ -142,6 +142,65 @@ def summarize_stats(stats_csv, out_md, command=""):
     print("\n".join(lines))
 
 
+def lmhead_bench(np, torch, tt, workloads, dev, B=32, S=16, H=4096, V=131072, iters=20, warm=20):
+    """The LM head fused with the unmask (tt_lmhead_unmask) at the unmask
+    workload's shape with a head of hidden size H_q * D = 4096, against the
+    same head as a library GEMM to fp32 logits followed by tt_unmask."""
+    rng = np.random.Generator(np.random.PCG64(57))
+    c = workloads.make_lmhead_case(rng, B, S, H, V, seed=57)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    hid, w = bf(c.hidden), bf(c.weight)
+    del c
+    mask = torch.ones((B, S), dtype=torch.uint8, device=dev)
+    ids = torch.empty((B, S), dtype=torch.int32, device=dev)
+    com = torch.empty((B, S), dtype=torch.uint8, device=dev)
+    conf = torch.empty((B, S), dtype=torch.float32, device=dev)
+    ws = torch.empty(tt.tt_lmhead_unmask_workspace_bytes(B, S, V, H), dtype=torch.uint8, device=dev)
+    uws = torch.empty(max(16, tt.tt_unmask_workspace_bytes(B, S, V)), dtype=torch.uint8, device=dev)
+
+    # both paths run warm-up calls first: the clock rises over the first tens
+    # of milliseconds of sustained matrix-core load
+    def timeit(f):
+        for _ in range(warm):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / iters
+
+    t_f = timeit(lambda: tt.tt_lmhead_unmask(hid, w, mask, None, 4, ids, com, conf, 0, ws))
+    wt = w.t()
+    try:
+        gemm = lambda: torch.mm(hid, wt, out_dtype=torch.float32)
+        gemm()
+        kind = "torch.mm bf16 -> fp32 (hipBLASLt)"
+    except Exception:
+        gemm = lambda: torch.mm(hid, wt).float()
+        kind = "torch.mm bf16 -> bf16, widened to fp32"
+    t_g = timeit(gemm)
+    logits = gemm().contiguous()
+    t_u = timeit(lambda: tt.tt_unmask(logits, mask, None, 4, ids, com, conf, 0, uws))
+    del logits
+    flops = 2.0 * B * S * H * V
+    log("lm head + unmask: fused %.1f us (%.0f TFLOP/s); unfused %.1f us (GEMM %.1f + unmask %.1f)"
+        % (t_f * 1e6, flops / t_f / 1e12, (t_g + t_u) * 1e6, t_g * 1e6, t_u * 1e6))
+    return {"us_per_call": t_f * 1e6, "TFLOP/s": flops / t_f / 1e12,
+            "frac_mfma": flops / t_f / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "weight_GB/s": V * H * 2 / t_f / 1e9,
+            "unfused_us": (t_g + t_u) * 1e6, "unfused_gemm_us": t_g * 1e6, "unfused_unmask_us": t_u * 1e6,
+            "unfused_gemm": kind, "speedup_vs_unfused": (t_g + t_u) / t_f,
+            "shape": "hidden [%d, %d] x head [%d, %d] bf16 -> ids/conf/commit (k = ceil(16/4))"
+                     % (B * S, H, V, H),
+            "weights": "synthetic: hidden ~ N(0,1), head ~ N(0, 9/H), so logits ~ N(0, 3^2)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +214,9 @@ def main():
     ap.add_argument("--core", action="store_true",
                     help="kernel-trace runs: the denoise loop and the attention timing only (no "
                          "chunk ingest, block sizes, threshold unmask or CPU baseline)")
+    ap.add_argument("--only-lmhead", action="store_true",
+                    help="kernel-trace runs: the fused LM head + unmask timing only (prints that "
+                         "section's JSON)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files into a summary")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
@@ -189,6 +251,10 @@ def main():
     tt.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only_lmhead:
+        print(json.dumps({"lmhead_unmask": lmhead_bench(np, torch, tt, workloads, dev)}), flush=True)
+        return
 
     t_gen = time.perf_counter()
     lp = workloads.config5(extra_blocks=1)
@@ -390,6 +456,7 @@ def main():
                "logits": "N(0, 3^2) fp32 [512, 131072] plus one seeded spike per row (peaked)"}
         log("threshold unmask: %.1f us/call, %.0f GB/s; sampler resolved the batch in %d steps "
             "(mean %.2f per sequence)" % (th_s * 1e6, th_gbs, sampler_steps, steps_per_seq.mean()))
+    lm = lmhead_bench(np, torch, tt, workloads, dev) if extras else None
     if args.only_attn:
         # calibration for FETCH_SIZE / WRITE_SIZE: a plain device copy of 256 MiB
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -468,6 +535,7 @@ def main():
         "unmask_threshold": thr,
         "chunk_attn": chunk,
         "block_sizes": block_sizes,
+        "lmhead_unmask": lm,
     }
     print(json.dumps(res), flush=True)
 
