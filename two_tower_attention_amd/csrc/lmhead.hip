@@ -12,23 +12,33 @@
 // (max, lowest index of the max, sum exp(l - max)); the unmask's merge and
 // commit kernels finish the rule.
 //
-// Work-group: 4 waves, one per SIMD (all 512 VGPRs of a lane are the wave's),
-// as a 2 x 2 grid of 128 x 128 wave tiles: wave (vw, rw) owns vocabulary rows
-// 128*vw.. and hidden rows 128*rw.. of the tile, 16 MFMA accumulator blocks
-// D[32 vocab][32 rows] (v_mfma_f32_32x32x16_bf16, A = weight rows, B =
-// hidden rows).  A lane then holds one hidden row of each block, so the
-// epilogue's row reductions are lane-local plus one lane-pair exchange.
+// Work-group: a 256 (vocabulary) x 256 (hidden rows) tile of logits^T, 4
+// waves, one per SIMD (so a wave may use all 512 registers of its lanes).
+// Wave w owns hidden rows 64*w .. 64*w+63 against all 256 weight rows: 16
+// MFMA accumulator blocks D[32 vocab][32 rows] (v_mfma_f32_32x32x16_bf16,
+// A = weight rows, B = hidden rows).  A lane then holds one hidden row of
+// every block, so the epilogue's row reductions are lane-local plus one
+// lane-pair exchange.
 //
-// Operands stream HBM -> LDS by direct loads through buffer descriptors into
-// a ring of kSlots stages; a stage is kKS reduction elements of the tile's
-// 256 weight rows and 256 hidden rows.  Small stages in many slots keep the
-// loads issued well ahead of their use (the ring's lead time is (kSlots - 2)
-// stages).  Inside a stage each row keeps its 16-byte chunks XOR-swizzled by
-// the row's position in its 256-byte group, which keeps the operand reads
-// (32 consecutive rows, one chunk) free of bank conflicts; each direct load
-// fills 1 KiB of rows, and a lane fetches whichever chunk the swizzle puts at
-// its slot.  One per-lane offset serves every load: load n of a tile adds its
-// first row as a scalar offset.
+// Operands.  The weight tile streams HBM -> LDS by direct loads through
+// buffer descriptors into a ring of 4 stages of 64 reduction elements (128
+// contiguous bytes of each of the 256 weight rows, 32 KiB); each 128-byte row
+// keeps its 16-byte chunks XOR-swizzled by bits 1..3 of the row index
+// (conflict-free operand reads).  A wave reads its 64 hidden rows only for
+// itself, so they skip LDS and go from memory straight into the MFMA operand
+// registers.  Loaded row-major, every such load would touch 32 rows (32
+// cache lines) for 1 KiB; a first kernel therefore copies the hidden state
+// once into fragment order (each 1 KiB MFMA operand contiguous), which costs
+// one pass over R*H*2 bytes.
+//
+// Pipeline.  Stage s issues, after the MFMAs of each step t, two weight loads
+// of stage s+3 and the hidden-row operands of step t of stage s+2, into the
+// registers that step t just consumed.  Memory loads complete in issue order
+// for the wait counter, so the wait for the hidden rows of step t, two stages
+// later, also covers the weight stage loaded alongside them: every load has
+// two stages to arrive, and the wait count is the same constant at every
+// step.  Loads past the last stage read through empty descriptors (zero, no
+// memory traffic), which keeps the counts uniform.
 #include <limits.h>
 
 #include "tt_internal.h"
@@ -36,35 +46,27 @@
 namespace tt {
 namespace {
 
-constexpr int kVT = 256;                        // vocabulary rows per work-group tile
-constexpr int kRT = 256;                        // hidden rows per work-group tile
-constexpr int kChunk = 128;                     // vocabulary entries per partial
-#ifndef TT_LM_KS
-#define TT_LM_KS 32
-#endif
-#ifndef TT_LM_SLOTS
-#define TT_LM_SLOTS 4
-#endif
-constexpr int kKS = TT_LM_KS;                   // reduction elements per stage
-constexpr int kSlots = TT_LM_SLOTS;             // ring stages
-constexpr int kThreads = 256;                   // 4 waves
-constexpr int kNCh = kKS / 8;                   // 16-byte chunks per row per stage
-constexpr int kSteps = kKS / 16;                // MFMA reduction steps per stage
-constexpr int kRowBytes = kKS * 2;              // bytes of one row per stage
-constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one 1 KiB direct load fills
-constexpr int kSwz = 16 / kNCh;                 // rows per 256 bytes: the swizzle's row period
-constexpr int kTileBytes = kVT * kRowBytes;     // one operand's part of a stage
-constexpr int kStageBytes = 2 * kTileBytes;     // weight part, then hidden part
-constexpr int kLoads = kTileBytes / 1024 / 4;   // 1 KiB loads per wave per operand per stage
-static_assert(kVT == kRT, "both operand parts of a stage have the same shape");
-static_assert(kKS == 16 || kKS == 32, "stage depth");
-static_assert(kLoads * 4 * 1024 == kTileBytes, "the waves share a stage's loads evenly");
-static_assert(kSlots >= 3 && (kSlots - 3) * 2 * kLoads < 64, "ring depth");
-static_assert(kSlots * kStageBytes <= 160 * 1024, "ring fits the LDS");
+constexpr int kVT = 256;                          // vocabulary rows per work-group tile
+constexpr int kRT = 256;                          // hidden rows per work-group tile
+constexpr int kWR = 64;                           // hidden rows per wave
+constexpr int kChunk = 128;                       // vocabulary entries per partial
+constexpr int kKS = 64;                           // reduction elements per stage
+constexpr int kSlots = 4;                         // weight ring stages
+constexpr int kThreads = 256;                     // 4 waves
+constexpr int kSteps = kKS / 16;                  // MFMA reduction steps per stage
+constexpr int kRowBytes = kKS * 2;                // 128 bytes of a weight row per stage
+constexpr int kRowsPerLoad = 1024 / kRowBytes;    // 8 rows per 1 KiB direct load
+constexpr int kStageBytes = kVT * kRowBytes;      // 32 KiB
+constexpr int kLoads = kStageBytes / 1024 / 4;    // weight loads per wave per stage
+constexpr int kXLoads = (kWR / 32) * kSteps;      // hidden-row loads per wave per stage
+constexpr int kFrag = 1024;                       // one MFMA operand of a wave: 64 lanes x 16 B
+static_assert(kLoads == 2 * kSteps, "two weight loads per reduction step");
+static_assert(kRT == 4 * kWR, "4 waves cover the row tile");
 
-// Physical 16-byte slot of logical chunk c in row r: XOR with the row's
-// position in its 256-byte group, so 16 consecutive rows cover all banks.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r / kSwz) % kNCh); }
+// Physical 16-byte slot of logical chunk c in weight row r: rows r and r + 2
+// share banks (128-byte rows), so the XOR runs over bits 1..3 of r and 16
+// consecutive rows cover all 64 banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -73,58 +75,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 }
 
 struct LmParams {
-  const __bf16 *x, *w;
-  UnmaskPart *parts;  // [R, NC]
+  const __bf16 *xp, *w;  // xp: hidden rows in fragment order
+  UnmaskPart *parts;     // [R, NC]
   int R, H, V, NC;
 };
 
-// Operands of one 16-element reduction step: 4 weight blocks, 4 hidden blocks.
-struct Ops {
-  bf16x8 w[4], x[4];
-};
-
-// Reads the wave's operands of one reduction step of a stage.  Row r of a
-// part keeps logical chunk c at r * kRowBytes + 16 * swz(r, c); the wave's
-// rows are 32*b + ln of its 128-row half, so the swizzle depends on ln only
-// and the block offset goes into the instruction's immediate.
-__device__ __forceinline__ void read_ops(const unsigned char *stage, unsigned lane_off, int vw,
-                                         int rw, Ops &o) {
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    o.w[b] = *(const bf16x8 *)(stage + (128 * vw + 32 * b) * kRowBytes + lane_off);
-    o.x[b] = *(const bf16x8 *)(stage + kTileBytes + (128 * rw + 32 * b) * kRowBytes + lane_off);
-  }
-}
-
-// The four MFMAs of weight block vb (128 cycles of matrix-core work).
-__device__ __forceinline__ void mfma_row(const Ops &o, int vb, f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-    acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.w[vb], o.x[rb], acc[vb][rb], 0, 0, 0);
+// Fragment order of the hidden state: for row tile rt, wave w, stage s,
+// step t and row block rb, one 1 KiB fragment whose lane l = 32*hl + ln holds
+// x[256*rt + 64*w + 32*rb + ln][64*s + 16*t + 8*hl .. +7], zero past R and
+// past H.  Fragment index ((((rt*4 + w)*nst + s)*kSteps + t)*2 + rb).
+__global__ __launch_bounds__(256) void lmhead_pack_kernel(const __bf16 *__restrict__ x,
+                                                          bf16x8 *__restrict__ xp, int R, int H,
+                                                          int nst, long long n16) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // 16-byte unit
+  if (i >= n16) return;
+  const int lane = (int)(i & 63);
+  long long f = i >> 6;
+  const int rb = (int)(f & 1);
+  f >>= 1;
+  const int t = (int)(f % kSteps);
+  f /= kSteps;
+  const int s = (int)(f % nst);
+  f /= nst;
+  const long long row = f * kWR + 32 * rb + (lane & 31);  // f = rt*4 + w
+  const int k = s * kKS + 16 * t + 8 * (lane >> 5);
+  bf16x8 v = {};
+  if (row < R && k < H) v = *(const bf16x8 *)(x + row * H + k);
+  xp[i] = v;
 }
 
 // lgkmcnt(0) only (gfx9 encoding): completes this wave's LDS reads.
 __device__ __forceinline__ void lds_wait() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
-// vmcnt(n) only.
 template <int N>
 __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-// Wait until at most `stages` stages of this wave's direct loads are in flight.
-template <int PER, int MAX>
-__device__ __forceinline__ void wait_stages(int stages) {
-  if constexpr (MAX > 0) {
-    if (stages >= MAX) {
-      vm_wait<PER * MAX>();
-      return;
-    }
-    wait_stages<PER, MAX - 1>(stages);
-  } else {
-    vm_wait<0>();
-  }
 }
 // Work-group barrier ordering LDS only (no global fence, which would drain
 // the direct loads still in flight).
@@ -135,12 +122,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+struct WOps {
+  bf16x8 v[8];  // weight blocks 0..7 of one reduction step
+};
+struct XOps {
+  bf16x8 v[kSteps][2];  // this wave's two hidden-row blocks, per step
+};
+
 __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
   extern __shared__ __align__(16) unsigned char ring[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 31, hl = lane >> 5;
-  const int vw = wave >> 1, rw = wave & 1;
+
   // Tile order.  Work-groups are dealt to the 8 XCDs round-robin (id % 8),
   // and each XCD has its own L2.  The row tiles of one vocabulary tile read
   // the same weight rows, so they go to ids 8 apart: same XCD, dispatched
@@ -160,148 +154,195 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
     vt = (nvt / 8) * 8 + j / nrt;
   }
   const int r0 = rt * kRT, v0 = vt * kVT;
-  const int w_rows = min(kVT, p.V - v0), x_rows = min(kRT, p.R - r0);
+  const int w_rows = min(kVT, p.V - v0);
   const __bf16 *wb = p.w + (size_t)v0 * p.H;
-  const __bf16 *xb = p.x + (size_t)r0 * p.H;
-  const int nst = p.H / kKS;
+  const int nst = (p.H + kKS - 1) / kKS;
 
-  // Direct loads: lane l of a load fills bytes 16l.. of 1 KiB = tile rows
-  // kRowsPerLoad*n + l/kNCh (n = the load), physical chunk l%kNCh, i.e. the
-  // logical chunk that swz() puts there; rows past the operand's end read as
-  // zero (descriptor range).  Load n adds n*kRowsPerLoad rows as a scalar
-  // offset, which leaves the swizzle unchanged (kRowsPerLoad is a multiple of
-  // its row period times kNCh).
-  static_assert(kRowsPerLoad % (kSwz * kNCh) == 0, "load boundaries keep the swizzle");
-  const int lrow = lane / kNCh;
-  const unsigned voff = (unsigned)((lrow * p.H + 8 * swz(lrow, lane % kNCh)) * 2);
-  // Load j (0 .. 2*kLoads-1) of this wave for stage s: weight part first.
-  // Issued one at a time between MFMA groups: the wave is the only one on
-  // its SIMD, and a load that waits for room in the memory queue holds up
-  // its instruction stream, so each load sits behind 128 cycles of queued
-  // matrix-core work instead of in a burst.
-  auto issue_one = [&](int s, int j) {
-    unsigned char *st = ring + (s % kSlots) * kStageBytes;
+  // Weight loads: load n = 8*wave + j of a stage fills tile rows 8n .. 8n+7
+  // (1 KiB); lane l holds row 8n + l/8, physical chunk l%8, i.e. logical
+  // chunk (l%8) ^ ((8n + l/8) >> 1 & 7), which depends on n only through
+  // j % 2.  One descriptor per wave and stage starts at the wave's first row
+  // (64*wave) and ends at the tile's last vocabulary row, and the per-lane
+  // offset carries the row, so rows past the vocabulary read as zero.
+  const int lrow = lane >> 3;
+  const int wrow0 = kLoads * kRowsPerLoad * wave;
+  unsigned voffw[2];
+  voffw[0] = (unsigned)((lrow * p.H + 8 * ((lane & 7) ^ ((lrow >> 1) & 7))) * 2);
+  voffw[1] = (unsigned)((lrow * p.H + 8 * ((lane & 7) ^ (((8 + lrow) >> 1) & 7))) * 2);
+  auto wrsrc = [&](int s) {
     const int k0 = s * kKS;
-    const bool wpart = j < kLoads;
-    const int n = kLoads * wave + (wpart ? j : j - kLoads);
-    const __amdgpu_buffer_rsrc_t r =
-        wpart ? buffer_rsrc(wb + k0, (w_rows * p.H - k0) * 2) : buffer_rsrc(xb + k0, (x_rows * p.H - k0) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(st + (wpart ? 0 : kTileBytes) + n * 1024), 16,
-                                             voff, (unsigned)(n * kRowsPerLoad * p.H * 2), 0, 0);
+    const int bytes = k0 < p.H ? max(0, ((w_rows - wrow0) * p.H - k0) * 2) : 0;
+    return buffer_rsrc(wb + (size_t)wrow0 * p.H + min(k0, p.H), bytes);
   };
-  auto issue = [&](int s) {
-    if (s >= nst) return;
+  auto wload = [&](const __amdgpu_buffer_rsrc_t &r, int s, int j) {
+    const int n = kLoads * wave + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(ring + (s % kSlots) * kStageBytes + n * 1024), 16,
+                                             voffw[j & 1] + (unsigned)(j * kRowsPerLoad * p.H * 2), 0, 0, 0);
+  };
+  // Hidden rows: this wave's fragments, stage after stage (8 KiB each); the
+  // descriptor ends after the last stage, so later stages read as zero.
+  const __amdgpu_buffer_rsrc_t xr =
+      buffer_rsrc(p.xp + (size_t)(rt * 4 + wave) * nst * (kXLoads * kFrag / 2), nst * kXLoads * kFrag);
+  auto xload = [&](int s, int t, XOps &x) {
 #pragma unroll
-    for (int j = 0; j < 2 * kLoads; ++j) issue_one(s, j);
+    for (int rb = 0; rb < 2; ++rb)
+      x.v[t][rb] = __builtin_bit_cast(
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                      xr, (unsigned)(16 * lane + ((s * kSteps + t) * 2 + rb) * kFrag), 0, 0));
   };
-  constexpr int kPer = 2 * kLoads;  // direct loads per wave per stage
 
-  // operand read offsets of this lane for reduction step t of a stage:
-  // row ln of a 32-row block, logical chunk 2*t + hl
+  // operand read offsets of this lane in a stage, step t: row ln of a 32-row
+  // block, logical chunk 2*t + hl (block b adds 4 KiB, an immediate)
   unsigned loff[kSteps];
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) loff[t] = (unsigned)(ln * kRowBytes + 16 * swz(ln, 2 * t + hl));
-
-  f32x16 acc[4][4];
+  auto wread = [&](int s, int t, WOps &o) {
+    const unsigned char *st = ring + (s % kSlots) * kStageBytes + loff[t];
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb)
+    for (int b = 0; b < 8; ++b) o.v[b] = *(const bf16x8 *)(st + b * 32 * kRowBytes);
+  };
+
+  f32x16 acc[8][2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) acc[vb][rb] = f32x16{};
+  for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[vb][rb] = f32x16{};
 
-  // Prologue: stages 0 .. kSlots-2 in flight, stage 0 landed and visible.
-  // In iteration s, stage s + 1 is awaited (it was issued kSlots - 3
-  // iterations earlier), so the operands of its first step can be read
-  // under the last MFMAs of stage s; stage s + kSlots - 1 then takes the
-  // slot of stage s - 1, which every wave has finished reading.
-  for (int s = 0; s < kSlots - 1; ++s) issue(s);
-  wait_stages<kPer, kSlots - 2>(min(kSlots - 2, nst - 1));
-  lds_barrier();
-  Ops buf[2];
-  read_ops(ring, loff[0], vw, rw, buf[0]);
-
-  // One stage: operands of its first step are in `cur`; the next stage's
-  // first operands end up in `cur` (two steps per stage) or `nxt` (one).
-  static_assert(2 * kLoads == 4 * kSteps, "one load per MFMA group");
-  auto stage = [&](int s, Ops &cur, Ops &nxt) {
-    if (s + 1 < nst) {
-      wait_stages<kPer, kSlots - 3>(min(kSlots - 3, nst - 2 - s));
-      lds_barrier();
-    }
-    const int sn = s + kSlots - 1;  // stage loaded into the slot of stage s - 1
-    const bool load = sn < nst;
-    const unsigned char *st = ring + (s % kSlots) * kStageBytes;
-    const unsigned char *st1 = ring + ((s + 1) % kSlots) * kStageBytes;
+  // Prologue: the loads that stages -3, -2 and -1 would have issued, in the
+  // same order: W(0); then per step t, W(1) loads 2t, 2t+1 and X(0) step t;
+  // the same for W(2) and X(1).
+  XOps xa, xb;
+  WOps wa, wb2;
+  {
+    const __amdgpu_buffer_rsrc_t r = wrsrc(0);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) wload(r, 0, j);
+  }
+#pragma unroll
+  for (int s = 1; s <= 2; ++s) {
+    const __amdgpu_buffer_rsrc_t r = wrsrc(s);
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
-      const Ops &o = t == 0 ? cur : nxt;
+      wload(r, s, 2 * t);
+      wload(r, s, 2 * t + 1);
+      xload(s - 1, t, s == 1 ? xa : xb);
+    }
+  }
+  vm_wait<2 * (kLoads + kXLoads)>();  // W(0)
+  lds_barrier();
+  wread(0, 0, wa);
+
+  // Loads issued per step: 2 weight + 2 hidden-row.  At step t of stage s the
+  // loads after X(s) step t are the rest of stage s-2 (steps t+1..3), all of
+  // stage s-1 and steps 0..t-1 of stage s: always 28.
+  constexpr int kPerStep = kLoads / kSteps + kXLoads / kSteps;
+  constexpr int kWaitX = kPerStep * (2 * kSteps - 1);
+  static_assert(kWaitX < 64, "vmcnt range");
+  auto stage = [&](int s, XOps &xc) {
+    const __amdgpu_buffer_rsrc_t rn = wrsrc(s + 3);
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      WOps &cur = (t & 1) ? wb2 : wa;
+      WOps &nxt = (t & 1) ? wa : wb2;
       lds_wait();
+      vm_wait<kWaitX>();  // X(s) step t; at t = 3 also W(s+1), loaded before it
+      if (t == kSteps - 1) {
+        // W(s+1) visible after the barrier, and every wave has finished
+        // reading W(s-1), whose slot W(s+3) takes
+        lds_barrier();
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < kSteps) read_ops(st, loff[t + 1], vw, rw, nxt);
-      else if (s + 1 < nst) read_ops(st1, loff[0], vw, rw, kSteps == 2 ? cur : nxt);
+      if (t + 1 < kSteps) wread(s, t + 1, nxt);
+      else wread(s + 1, 0, nxt);  // after the last stage: an unused read
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
-        mfma_row(o, vb, acc);
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int vb = 4 * half; vb < 4 * half + 4; ++vb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[vb], xc.v[t][rb], acc[vb][rb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (load) issue_one(sn, 4 * t + vb);
+        wload(rn, s + 3, 2 * t + half);
         __builtin_amdgcn_sched_barrier(0);
       }
+      xload(s + 2, t, xc);  // into the registers this step consumed
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int s = 0; s < nst; ++s) {
-    stage(s, buf[0], buf[1]);
-    if (kSteps == 1) buf[0] = buf[1];  // register moves, under the MFMAs
+  // two stages per iteration: xa holds the hidden rows of even stages, xb of
+  // odd ones; the next weight operands always sit in wa (kSteps is even).
+  // An odd stage count gets one more stage, whose operands read as zero.
+  for (int s = 0; s < nst; s += 2) {
+    stage(s, xa);
+    stage(s + 1, xb);
   }
+  // the loads past the last stage complete before the work-group's LDS is
+  // released
+  vm_wait<0>();
 
   // Epilogue.  Accumulator register q of lane (hl, ln) in block (vb, rb)
   // holds the logit of vocabulary entry 32*vb + 8*(q/4) + 4*hl + q%4 of the
-  // wave's half and hidden row 32*rb + ln of its half.  Per row: max and
-  // lowest index over the lane's 64 entries, then over the lane pair
-  // (l, l ^ 32), then sum exp(l - max) the same way.
-  const int vbase = v0 + 128 * vw;
-  if (vbase >= p.V) return;  // this wave's half lies past the vocabulary
-  const int chunk = vbase / kChunk;
+  // tile and hidden row 64*wave + 32*rb + ln of the tile.  Per row and
+  // 128-entry chunk (blocks 4*hc .. 4*hc+3): max and lowest index over the
+  // lane's 64 entries, then over the lane pair (l, l ^ 32), then sum
+  // exp(l - max) the same way.
   constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    float m = -INFINITY;
-    int idx = INT_MAX;
+  for (int hc = 0; hc < 2; ++hc) {
+    const int vbase = v0 + kChunk * hc;
+    if (vbase >= p.V) break;
+    if (vbase + kChunk > p.V) {
+      // ragged last chunk: entries past the vocabulary become -inf, which
+      // neither the max nor the sum sees
+      const int lim = p.V - vbase;
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+      for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int v = vbase + 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
-        const float l = acc[vb][rb][q];
-        if (v < p.V && l > m) {  // entries visited in increasing v: keeps the lowest
-          m = l;
-          idx = v;
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int off = 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
+            if (off >= lim) acc[4 * hc + vb][rb][q] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float m = -INFINITY;
+      int idx = INT_MAX;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const float l = acc[4 * hc + vb][rb][q];
+          if (l > m) {  // entries visited in increasing order: keeps the lowest
+            m = l;
+            idx = vbase + 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
+          }
         }
-      }
-    auto mi = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    auto ii = __builtin_amdgcn_permlane32_swap((unsigned)idx, (unsigned)idx, false, false);
-    const float ma = __uint_as_float(mi[0]), mb = __uint_as_float(mi[1]);
-    const int ia = (int)ii[0], ib = (int)ii[1];
-    const float M = fmaxf(ma, mb);
-    const int I = min(ma == M ? ia : INT_MAX, mb == M ? ib : INT_MAX);
-    float sum = 0.f;
+      auto mi = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      auto ii = __builtin_amdgcn_permlane32_swap((unsigned)idx, (unsigned)idx, false, false);
+      const float ma = __uint_as_float(mi[0]), mb = __uint_as_float(mi[1]);
+      const int ia = (int)ii[0], ib = (int)ii[1];
+      const float M = fmaxf(ma, mb);
+      const int I = min(ma == M ? ia : INT_MAX, mb == M ? ib : INT_MAX);
+      float sum = 0.f;
 #pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
+      for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int v = vbase + 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
-        const float e = __builtin_amdgcn_exp2f((acc[vb][rb][q] - M) * kLog2e);
-        sum += v < p.V ? e : 0.f;
+        for (int q = 0; q < 16; ++q)
+          sum += __builtin_amdgcn_exp2f((acc[4 * hc + vb][rb][q] - M) * kLog2e);
+      auto si = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+      const float S = __uint_as_float(si[0]) + __uint_as_float(si[1]);
+      const int row = r0 + kWR * wave + 32 * rb + ln;
+      if (hl == 0 && row < p.R) {
+        UnmaskPart pt;
+        pt.m = M;
+        pt.s = S;
+        pt.idx = I;
+        pt.pad = 0;
+        p.parts[(size_t)row * p.NC + vbase / kChunk] = pt;
       }
-    auto si = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
-    const float S = __uint_as_float(si[0]) + __uint_as_float(si[1]);
-    const int row = r0 + 128 * rw + 32 * rb + ln;
-    if (hl == 0 && row < p.R) {
-      UnmaskPart pt;
-      pt.m = M;
-      pt.s = S;
-      pt.idx = I;
-      pt.pad = 0;
-      p.parts[(size_t)row * p.NC + chunk] = pt;
     }
   }
 }
@@ -310,8 +351,13 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
 
 int lmhead_chunks(int V) { return (V + kChunk - 1) / kChunk; }
 
+size_t lmhead_pack_bytes(int R, int H) {
+  const size_t nrt = (size_t)(R + kRT - 1) / kRT, nst = (size_t)(H + kKS - 1) / kKS;
+  return nrt * 4 * nst * kXLoads * kFrag;
+}
+
 hipError_t launch_lmhead_parts(const void *hidden, const void *weight, int R, int H, int V,
-                               UnmaskPart *parts, hipStream_t stream) {
+                               UnmaskPart *parts, void *xpack, hipStream_t stream) {
   static bool attr_done = false;  // benign race: every caller sets the same value
   if (!attr_done) {
     const hipError_t e = hipFuncSetAttribute((const void *)lmhead_kernel,
@@ -320,8 +366,12 @@ hipError_t launch_lmhead_parts(const void *hidden, const void *weight, int R, in
     if (e != hipSuccess) return e;
     attr_done = true;
   }
+  const int nst = (H + kKS - 1) / kKS;
+  const long long n16 = (long long)(lmhead_pack_bytes(R, H) / 16);
+  hipLaunchKernelGGL(lmhead_pack_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream,
+                     (const __bf16 *)hidden, (bf16x8 *)xpack, R, H, nst, n16);
   LmParams prm;
-  prm.x = (const __bf16 *)hidden;
+  prm.xp = (const __bf16 *)xpack;
   prm.w = (const __bf16 *)weight;
   prm.parts = parts;
   prm.R = R;

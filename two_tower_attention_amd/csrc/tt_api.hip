@@ -282,18 +282,22 @@ static int check_lmhead_shape(int32_t B, int32_t S, int32_t V, int32_t H) {
 
 static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// parts [R, chunks] then the merged row partials [R]
-static size_t lmhead_ws_bytes(int32_t B, int32_t S, int32_t V) {
+// parts [R, chunks], the merged row partials [R], then the hidden state in
+// MFMA fragment order
+static size_t lmhead_parts_bytes(int32_t B, int32_t S, int32_t V) {
+  return round256((size_t)B * S * tt::lmhead_chunks(V) * sizeof(tt::UnmaskPart));
+}
+static size_t lmhead_ws_bytes(int32_t B, int32_t S, int32_t V, int32_t H) {
   const size_t R = (size_t)B * S;
-  return round256(R * tt::lmhead_chunks(V) * sizeof(tt::UnmaskPart)) +
-         round256(R * sizeof(tt::UnmaskPart));
+  return lmhead_parts_bytes(B, S, V) + round256(R * sizeof(tt::UnmaskPart)) +
+         round256(tt::lmhead_pack_bytes((int)R, H));
 }
 
 int tt_lmhead_unmask_workspace_bytes(int32_t B, int32_t S, int32_t V, int32_t H, size_t *bytes) {
   if (!bytes) return fail(TT_ERR_NULL, "bytes is NULL");
   const int st = check_lmhead_shape(B, S, V, H);
   if (st) return st;
-  *bytes = B == 0 ? 0 : lmhead_ws_bytes(B, S, V);
+  *bytes = B == 0 ? 0 : lmhead_ws_bytes(B, S, V, H);
   return ok();
 }
 
@@ -305,7 +309,7 @@ static int lmhead_rows(const void *hidden, const void *weight, int32_t B, int32_
   if (!hidden || !weight) return fail(TT_ERR_NULL, "hidden and weight are required");
   if (!aligned(hidden, 16) || !aligned(weight, 16))
     return fail(TT_ERR_UNSUPPORTED, "hidden and weight must be 16-byte aligned");
-  const size_t need = lmhead_ws_bytes(B, S, V);
+  const size_t need = lmhead_ws_bytes(B, S, V, H);
   if (!workspace || workspace_bytes < need)
     return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -313,9 +317,10 @@ static int lmhead_rows(const void *hidden, const void *weight, int32_t B, int32_
   if (device_cus(nullptr) <= 0) return fail(TT_ERR_NO_DEVICE, "no HIP device");
   const int R = B * S;
   tt::UnmaskPart *parts = (tt::UnmaskPart *)workspace;
-  *merged = (tt::UnmaskPart *)((unsigned char *)workspace +
-                               round256((size_t)R * tt::lmhead_chunks(V) * sizeof(tt::UnmaskPart)));
-  hipError_t e = tt::launch_lmhead_parts(hidden, weight, R, H, V, parts, s);
+  *merged = (tt::UnmaskPart *)((unsigned char *)workspace + lmhead_parts_bytes(B, S, V));
+  void *xpack = (unsigned char *)workspace + lmhead_parts_bytes(B, S, V) +
+                round256((size_t)R * sizeof(tt::UnmaskPart));
+  hipError_t e = tt::launch_lmhead_parts(hidden, weight, R, H, V, parts, xpack, s);
   if (e == hipSuccess) e = tt::launch_unmask_merge(parts, tt::lmhead_chunks(V), R, *merged, s);
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return TT_OK;

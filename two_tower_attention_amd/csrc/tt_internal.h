@@ -90,8 +90,11 @@ hipError_t launch_unmask_threshold_commit(const UnmaskPart *parts, int chunks, i
 
 // LM head fused with the unmask's row reduction: hidden [R, H] and weight
 // [V, H] in bf16 -> per (row, 128-vocabulary chunk) partials [R, lmhead_chunks(V)].
+// xpack: lmhead_pack_bytes(R, H) bytes of scratch (16-byte aligned) for the
+// hidden state in MFMA fragment order.
 int lmhead_chunks(int V);
+size_t lmhead_pack_bytes(int R, int H);
 hipError_t launch_lmhead_parts(const void *hidden, const void *weight, int R, int H, int V,
-                               UnmaskPart *parts, hipStream_t stream);
+                               UnmaskPart *parts, void *xpack, hipStream_t stream);
 
 }  // namespace tt
