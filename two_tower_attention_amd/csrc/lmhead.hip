@@ -49,7 +49,7 @@ namespace {
 constexpr int kVT = 256;                          // vocabulary rows per work-group tile
 constexpr int kRT = 256;                          // hidden rows per work-group tile
 constexpr int kWR = 64;                           // hidden rows per wave
-constexpr int kChunk = 128;                       // vocabulary entries per partial
+constexpr int kChunk = kVT;                       // vocabulary entries per partial (one tile)
 constexpr int kKS = 64;                           // reduction elements per stage
 constexpr int kSlots = 4;                         // weight ring stages
 constexpr int kThreads = 256;                     // 4 waves
@@ -183,12 +183,10 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
   // descriptor ends after the last stage, so later stages read as zero.
   const __amdgpu_buffer_rsrc_t xr =
       buffer_rsrc(p.xp + (size_t)(rt * 4 + wave) * nst * (kXLoads * kFrag / 2), nst * kXLoads * kFrag);
-  auto xload = [&](int s, int t, XOps &x) {
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      x.v[t][rb] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                      xr, (unsigned)(16 * lane + ((s * kSteps + t) * 2 + rb) * kFrag), 0, 0));
+  auto xload = [&](int s, int t, int rb, XOps &x) {
+    x.v[t][rb] = __builtin_bit_cast(
+        bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, (unsigned)(16 * lane + ((s * kSteps + t) * 2 + rb) * kFrag),
+                                                      0, 0));
   };
 
   // operand read offsets of this lane in a stage, step t: row ln of a 32-row
@@ -196,10 +194,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
   unsigned loff[kSteps];
 #pragma unroll
   for (int t = 0; t < kSteps; ++t) loff[t] = (unsigned)(ln * kRowBytes + 16 * swz(ln, 2 * t + hl));
+  auto wread1 = [&](int s, int t, int b, WOps &o) {
+    o.v[b] = *(const bf16x8 *)(ring + (s % kSlots) * kStageBytes + loff[t] + b * 32 * kRowBytes);
+  };
   auto wread = [&](int s, int t, WOps &o) {
-    const unsigned char *st = ring + (s % kSlots) * kStageBytes + loff[t];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) o.v[b] = *(const bf16x8 *)(st + b * 32 * kRowBytes);
+    for (int b = 0; b < 8; ++b) wread1(s, t, b, o);
   };
 
   f32x16 acc[8][2];
@@ -224,17 +224,23 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
 #pragma unroll
     for (int t = 0; t < kSteps; ++t) {
       wload(r, s, 2 * t);
+      xload(s - 1, t, 0, s == 1 ? xa : xb);
       wload(r, s, 2 * t + 1);
-      xload(s - 1, t, s == 1 ? xa : xb);
+      xload(s - 1, t, 1, s == 1 ? xa : xb);
     }
   }
   vm_wait<2 * (kLoads + kXLoads)>();  // W(0)
   lds_barrier();
   wread(0, 0, wa);
 
-  // Loads issued per step: 2 weight + 2 hidden-row.  At step t of stage s the
-  // loads after X(s) step t are the rest of stage s-2 (steps t+1..3), all of
-  // stage s-1 and steps 0..t-1 of stage s: always 28.
+  // Per step: 16 MFMAs (row block 0 first), the next step's 8 weight operand
+  // reads one after each of the first 8 MFMAs, and one memory load after
+  // every 4 MFMAs, alternating weight and hidden-row (a load waits for room
+  // in the memory queue, and the wave is the only one on its SIMD, so loads
+  // go where matrix work is queued, never in bursts).  The hidden-row load
+  // of row block rb follows the last MFMA that reads it.  At step t of stage
+  // s the loads after X(s) step t are the rest of stage s-2 (steps t+1..3),
+  // all of stage s-1 and steps 0..t-1 of stage s: always 28.
   constexpr int kPerStep = kLoads / kSteps + kXLoads / kSteps;
   constexpr int kWaitX = kPerStep * (2 * kSteps - 1);
   static_assert(kWaitX < 64, "vmcnt range");
@@ -251,23 +257,19 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
         // reading W(s-1), whose slot W(s+3) takes
         lds_barrier();
       }
+      // the next step's operands: this stage's, or the next stage's first
+      // (after the last stage an unused read)
+      const int rs = t + 1 < kSteps ? s : s + 1, rstep = (t + 1) % kSteps;
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < kSteps) wread(s, t + 1, nxt);
-      else wread(s + 1, 0, nxt);  // after the last stage: an unused read
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int vb = 4 * half; vb < 4 * half + 4; ++vb)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[vb], xc.v[t][rb], acc[vb][rb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        wload(rn, s + 3, 2 * t + half);
+      for (int m = 0; m < 16; ++m) {
+        const int rb = m >> 3, vb = m & 7;
+        acc[vb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.v[vb], xc.v[t][rb], acc[vb][rb], 0, 0, 0);
+        if (m < 8) wread1(rs, rstep, m, nxt);
+        if ((m & 7) == 3) wload(rn, s + 3, 2 * t + rb);
+        if ((m & 7) == 7) xload(s + 2, t, rb, xc);  // into the registers just consumed
         __builtin_amdgcn_sched_barrier(0);
       }
-      xload(s + 2, t, xc);  // into the registers this step consumed
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // two stages per iteration: xa holds the hidden rows of even stages, xb of
@@ -283,67 +285,59 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
 
   // Epilogue.  Accumulator register q of lane (hl, ln) in block (vb, rb)
   // holds the logit of vocabulary entry 32*vb + 8*(q/4) + 4*hl + q%4 of the
-  // tile and hidden row 64*wave + 32*rb + ln of the tile.  Per row and
-  // 128-entry chunk (blocks 4*hc .. 4*hc+3): max and lowest index over the
-  // lane's 64 entries, then over the lane pair (l, l ^ 32), then sum
-  // exp(l - max) the same way.
+  // tile and hidden row 64*wave + 32*rb + ln of the tile.  Per row: max and
+  // lowest index over the lane's 128 entries, then over the lane pair
+  // (l, l ^ 32), then sum exp(l - max) the same way; one partial per row and
+  // vocabulary tile.  Entries past the vocabulary (a ragged last tile) count
+  // as -inf.
   constexpr float kLog2e = 1.4426950408889634f;
+  const int lim = p.V - v0;
+  __builtin_amdgcn_sched_barrier(0);
+  if (lim < kVT) {
 #pragma unroll
-  for (int hc = 0; hc < 2; ++hc) {
-    const int vbase = v0 + kChunk * hc;
-    if (vbase >= p.V) break;
-    if (vbase + kChunk > p.V) {
-      // ragged last chunk: entries past the vocabulary become -inf, which
-      // neither the max nor the sum sees
-      const int lim = p.V - vbase;
+    for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int off = 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
-            if (off >= lim) acc[4 * hc + vb][rb][q] = -INFINITY;
-          }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      float m = -INFINITY;
-      int idx = INT_MAX;
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const float l = acc[4 * hc + vb][rb][q];
-          if (l > m) {  // entries visited in increasing order: keeps the lowest
-            m = l;
-            idx = vbase + 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
-          }
-        }
-      auto mi = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-      auto ii = __builtin_amdgcn_permlane32_swap((unsigned)idx, (unsigned)idx, false, false);
-      const float ma = __uint_as_float(mi[0]), mb = __uint_as_float(mi[1]);
-      const int ia = (int)ii[0], ib = (int)ii[1];
-      const float M = fmaxf(ma, mb);
-      const int I = min(ma == M ? ia : INT_MAX, mb == M ? ib : INT_MAX);
-      float sum = 0.f;
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-          sum += __builtin_amdgcn_exp2f((acc[4 * hc + vb][rb][q] - M) * kLog2e);
-      auto si = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
-      const float S = __uint_as_float(si[0]) + __uint_as_float(si[1]);
-      const int row = r0 + kWR * wave + 32 * rb + ln;
-      if (hl == 0 && row < p.R) {
-        UnmaskPart pt;
-        pt.m = M;
-        pt.s = S;
-        pt.idx = I;
-        pt.pad = 0;
-        p.parts[(size_t)row * p.NC + vbase / kChunk] = pt;
-      }
+          if (32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3) >= lim) acc[vb][rb][q] = -INFINITY;
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    __builtin_amdgcn_sched_barrier(0);
+    float m = -INFINITY;
+    int idx = INT_MAX;
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (acc[vb][rb][q] > m) {  // entries visited in increasing order: keeps the lowest
+          m = acc[vb][rb][q];
+          idx = v0 + 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
+        }
+    auto mi = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    auto ii = __builtin_amdgcn_permlane32_swap((unsigned)idx, (unsigned)idx, false, false);
+    const float ma = __uint_as_float(mi[0]), mb = __uint_as_float(mi[1]);
+    const int ia = (int)ii[0], ib = (int)ii[1];
+    const float M = fmaxf(ma, mb);
+    const int I = min(ma == M ? ia : INT_MAX, mb == M ? ib : INT_MAX);
+    float sum = 0.f;
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sum += __builtin_amdgcn_exp2f((acc[vb][rb][q] - M) * kLog2e);
+    auto si = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+    const float S = __uint_as_float(si[0]) + __uint_as_float(si[1]);
+    const int row = r0 + kWR * wave + 32 * rb + ln;
+    if (hl == 0 && row < p.R) {
+      UnmaskPart pt;
+      pt.m = M;
+      pt.s = S;
+      pt.idx = I;
+      pt.pad = 0;
+      p.parts[(size_t)row * p.NC + vt] = pt;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
