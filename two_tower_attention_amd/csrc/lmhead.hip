@@ -41,6 +41,8 @@
 // memory traffic), which keeps the counts uniform.
 #include <limits.h>
 
+#include <type_traits>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -292,29 +294,24 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
   // as -inf.
   constexpr float kLog2e = 1.4426950408889634f;
   const int lim = p.V - v0;
-  __builtin_amdgcn_sched_barrier(0);
-  if (lim < kVT) {
-#pragma unroll
-    for (int vb = 0; vb < 8; ++vb)
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-          if (32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3) >= lim) acc[vb][rb][q] = -INFINITY;
-  }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    __builtin_amdgcn_sched_barrier(0);
+  auto reduce = [&](int rb, auto ragged) {
+    constexpr bool kRagged = decltype(ragged)::value;
+    auto val = [&](int vb, int q) {
+      const float l = acc[vb][rb][q];
+      return !kRagged || 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3) < lim ? l : -INFINITY;
+    };
     float m = -INFINITY;
     int idx = INT_MAX;
 #pragma unroll
     for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (acc[vb][rb][q] > m) {  // entries visited in increasing order: keeps the lowest
-          m = acc[vb][rb][q];
+      for (int q = 0; q < 16; ++q) {
+        const float l = val(vb, q);
+        if (l > m) {  // entries visited in increasing order: keeps the lowest
+          m = l;
           idx = v0 + 32 * vb + 8 * (q >> 2) + 4 * hl + (q & 3);
         }
+      }
     auto mi = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
     auto ii = __builtin_amdgcn_permlane32_swap((unsigned)idx, (unsigned)idx, false, false);
     const float ma = __uint_as_float(mi[0]), mb = __uint_as_float(mi[1]);
@@ -325,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
 #pragma unroll
     for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) sum += __builtin_amdgcn_exp2f((acc[vb][rb][q] - M) * kLog2e);
+      for (int q = 0; q < 16; ++q) sum += __builtin_amdgcn_exp2f((val(vb, q) - M) * kLog2e);
     auto si = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
     const float S = __uint_as_float(si[0]) + __uint_as_float(si[1]);
     const int row = r0 + kWR * wave + 32 * rb + ln;
@@ -337,7 +334,13 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_kernel(LmParams p) {
       pt.pad = 0;
       p.parts[(size_t)row * p.NC + vt] = pt;
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (lim >= kVT) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) reduce(rb, std::false_type{});
+  } else {  // the ragged last tile: entries past the vocabulary count as -inf
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) reduce(rb, std::true_type{});
   }
 }
 
