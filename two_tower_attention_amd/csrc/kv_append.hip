@@ -5,9 +5,8 @@
 // logical positions L_b .. L_b+S-1, then advances ctx_lens[b].  Pure data
 // movement, bit-exact.
 //
-// Grid (B, H_kv), one work-group per (sequence, KV head).  Every head reads
-// L_b, so the length update runs afterwards in a second kernel (one thread
-// per sequence) on the same stream.
+// One work-group per sequence covers all its KV heads, so it can advance
+// ctx_lens[b] itself once every thread has read L_b (no second launch).
 #include "tt_internal.h"
 
 namespace tt {
@@ -33,50 +32,68 @@ __device__ __forceinline__ bool target_ok(const AppendParams &p, int b, int L) {
   return true;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
-  const int b = blockIdx.x, h = blockIdx.y;
-  const int L = p.ctx_lens[b];
-  if (!target_ok(p, b, L)) return;
-  const int32_t *pt = p.page_table + (size_t)b * p.max_pages;
-  T *kp = (T *)p.k_pages;
-  T *vp = (T *)p.v_pages;
-  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
-  const int chunks = p.D / VEC;        // D is a multiple of VEC on the vector path
-  if (p.vec && p.D % VEC == 0) {
-    // keys: one 16-byte chunk per thread iteration
-    for (int e = threadIdx.x; e < p.S * chunks; e += kThreads) {
-      const int t = e / chunks, c = e % chunks;
-      const int pos = L + t;
-      const size_t pg = (size_t)pt[pos / p.page_size];
-      const uint4 x = *(const uint4 *)((const T *)p.k_blk + (((size_t)b * p.S + t) * p.Hkv + h) * p.D + VEC * c);
-      *(uint4 *)(kp + ((pg * p.Hkv + h) * p.page_size + pos % p.page_size) * p.D + VEC * c) = x;
-    }
-  } else {
-    for (int e = threadIdx.x; e < p.S * p.D; e += kThreads) {
-      const int t = e / p.D, d = e % p.D;
-      const int pos = L + t;
-      const size_t pg = (size_t)pt[pos / p.page_size];
-      kp[((pg * p.Hkv + h) * p.page_size + pos % p.page_size) * p.D + d] =
-          ((const T *)p.k_blk)[(((size_t)b * p.S + t) * p.Hkv + h) * p.D + d];
-    }
-  }
-  // values: thread = (feature d, token t); consecutive threads write consecutive
-  // slots of one feature row of the page
-  for (int e = threadIdx.x; e < p.S * p.D; e += kThreads) {
-    const int d = e / p.S, t = e % p.S;
-    const int pos = L + t;
-    const size_t pg = (size_t)pt[pos / p.page_size];
-    vp[((pg * p.Hkv + h) * p.D + d) * p.page_size + pos % p.page_size] =
-        ((const T *)p.v_blk)[(((size_t)b * p.S + t) * p.Hkv + h) * p.D + d];
-  }
+// LDS bytes of a pass: the values of `hp` heads, [S][hp][D]
+constexpr int kStageBytes = 32 * 1024;
+__host__ __device__ inline int heads_per_pass(int S, int Hkv, int D, int elem) {
+  const int hp = kStageBytes / (S * D * elem);
+  return hp < 1 ? 1 : hp > Hkv ? Hkv : hp;
 }
 
-__global__ __launch_bounds__(kThreads) void advance_lens_kernel(AppendParams p) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= p.B) return;
+template <typename T>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T *sv = (T *)smem;  // values of the pass's heads [S][hp][D]
+  const int b = blockIdx.x;
   const int L = p.ctx_lens[b];
-  if (target_ok(p, b, L)) p.ctx_lens[b] = L + p.S;
+  if (!target_ok(p, b, L)) return;  // uniform over the work-group
+  const int32_t *__restrict__ pt = p.page_table + (size_t)b * p.max_pages;
+  const T *__restrict__ kb = (const T *)p.k_blk + (size_t)b * p.S * p.Hkv * p.D;
+  const T *__restrict__ vb = (const T *)p.v_blk + (size_t)b * p.S * p.Hkv * p.D;
+  T *__restrict__ kp = (T *)p.k_pages;
+  T *__restrict__ vp = (T *)p.v_pages;
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
+  const bool vec = p.vec && p.D % VEC == 0;
+  const int hp = heads_per_pass(p.S, p.Hkv, p.D, (int)sizeof(T));
+  for (int h0 = 0; h0 < p.Hkv; h0 += hp) {
+    const int nh = min(hp, p.Hkv - h0);
+    const int row = nh * p.D;  // elements of one token's row in this pass
+    if (vec) {
+      // keys: token rows, 16-byte chunks straight to their page rows; values:
+      // the same rows into LDS
+      const int chunks = row / VEC;
+      for (int e = threadIdx.x; e < p.S * chunks; e += kThreads) {
+        const int t = e / chunks, c = e % chunks;
+        const int hh = (VEC * c) / p.D, d = (VEC * c) % p.D;
+        const size_t src = ((size_t)t * p.Hkv + h0) * p.D + VEC * c;
+        const uint4 k = *(const uint4 *)(kb + src);
+        const uint4 v = *(const uint4 *)(vb + src);
+        const int pos = L + t;
+        const size_t pg = (size_t)pt[pos / p.page_size];
+        *(uint4 *)(kp + ((pg * p.Hkv + h0 + hh) * p.page_size + pos % p.page_size) * p.D + d) = k;
+        *(uint4 *)(sv + t * row + VEC * c) = v;
+      }
+    } else {
+      for (int e = threadIdx.x; e < p.S * row; e += kThreads) {
+        const int t = e / row, j = e % row, hh = j / p.D, d = j % p.D;
+        const size_t src = ((size_t)t * p.Hkv + h0) * p.D + j;
+        const int pos = L + t;
+        const size_t pg = (size_t)pt[pos / p.page_size];
+        kp[((pg * p.Hkv + h0 + hh) * p.page_size + pos % p.page_size) * p.D + d] = kb[src];
+        sv[t * row + j] = vb[src];
+      }
+    }
+    __syncthreads();
+    // values: thread = (head, feature, token), token fastest, so consecutive
+    // threads write consecutive slots of one feature row of the page
+    for (int e = threadIdx.x; e < p.S * row; e += kThreads) {
+      const int j = e / p.S, t = e % p.S, hh = j / p.D, d = j % p.D;
+      const int pos = L + t;
+      const size_t pg = (size_t)pt[pos / p.page_size];
+      vp[((pg * p.Hkv + h0 + hh) * p.D + d) * p.page_size + pos % p.page_size] = sv[t * row + j];
+    }
+    __syncthreads();  // sv is refilled by the next pass; every thread has read L_b
+  }
+  if (threadIdx.x == 0) p.ctx_lens[b] = L + p.S;  // only this work-group touches sequence b
 }
 
 }  // namespace
@@ -90,15 +107,16 @@ hipError_t launch_kv_append(const tt_attn_desc &d, const void *k_blk, const void
   p.B = d.batch; p.S = d.block; p.Hkv = d.heads_kv; p.D = d.head_dim; p.page_size = d.page_size;
   p.max_pages = d.max_pages_per_seq; p.num_pages = d.num_pages;
   p.vec = ((uintptr_t)k_blk % 16 == 0) && ((uintptr_t)k_pages % 16 == 0);
-  const dim3 grid(d.batch, d.heads_kv);
+  if (d.batch == 0) return hipSuccess;
+  // the values of one pass's heads staged in LDS (at most 32 KiB: one head
+  // is at most 64 * 128 * 4 bytes)
+  const int elem = d.dtype == TT_BF16 ? 2 : 4;
+  const size_t lds = (size_t)d.block * d.head_dim * elem *
+                     heads_per_pass(d.block, d.heads_kv, d.head_dim, elem);
   if (d.dtype == TT_BF16)
-    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3(d.batch), dim3(kThreads), lds, stream, p);
   else
-    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(kThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(advance_lens_kernel, dim3((d.batch + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, p);
+    hipLaunchKernelGGL(kv_append_kernel<float>, dim3(d.batch), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
