@@ -34,6 +34,45 @@ def test_kv_append_bit_exact(dtype, ps, lens):
     assert np.array_equal(_bits(dc.v_pages, dtype).view(np.uint8), vp.view(np.uint8))
 
 
+@pytest.mark.parametrize("dtype,S,Hkv,D,lens", [
+    ("bf16", 64, 3, 128, [0, 200, 300]),   # one head is 16 KiB: passes of 2 heads, then 1
+    ("f32", 64, 3, 128, [64, 5, 511]),     # one head is 32 KiB: one head per pass
+    ("bf16", 1, 5, 64, [0, 255, 256]),     # a one-token block, all 5 heads in one pass
+])
+def test_kv_append_head_passes(dtype, S, Hkv, D, lens):
+    """Bit-exact append when the heads' values do not fit one LDS pass."""
+    import two_tower_attention_amd as tt
+    rng = np.random.Generator(np.random.PCG64(S * 100 + Hkv * 10 + D))
+    c = workloads.make_attn_case(rng, B=len(lens), S=S, Hq=Hkv, Hkv=Hkv, D=D, ctx_lens=lens,
+                                 page_size=256, dtype=dtype, extra_tokens=S)
+    dc = DevCase(c)
+    tt.tt_kv_append(dc.desc, dc.k_blk, dc.v_blk, dc.k_pages, dc.v_pages, dc.page_table, dc.ctx_lens)
+    kp, vp, nl = oracle.kv_append(c.k_pages, c.v_pages, c.page_table, c.ctx_lens, c.k_blk, c.v_blk)
+    assert np.array_equal(dc.ctx_lens.cpu().numpy(), nl)
+    assert np.array_equal(_bits(dc.k_pages, dtype).view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_bits(dc.v_pages, dtype).view(np.uint8), vp.view(np.uint8))
+
+
+def test_kv_append_unaligned_block():
+    """Block keys that start off a 16-byte boundary take the element-wise path."""
+    import two_tower_attention_amd as tt
+    torch = torch_mod()
+    rng = np.random.Generator(np.random.PCG64(21))
+    c = workloads.make_attn_case(rng, B=2, S=16, Hq=4, Hkv=2, D=64, ctx_lens=[7, 300],
+                                 page_size=256, extra_tokens=16)
+    dc = DevCase(c)
+    n = dc.k_blk.numel()
+    buf = torch.empty(n + 1, dtype=dc.k_blk.dtype, device=dc.k_blk.device)
+    k_off = buf[1:].view(dc.k_blk.shape)   # 2 bytes past a 16-byte boundary
+    k_off.copy_(dc.k_blk)
+    assert k_off.data_ptr() % 16 != 0
+    tt.tt_kv_append(dc.desc, k_off, dc.v_blk, dc.k_pages, dc.v_pages, dc.page_table, dc.ctx_lens)
+    kp, vp, nl = oracle.kv_append(c.k_pages, c.v_pages, c.page_table, c.ctx_lens, c.k_blk, c.v_blk)
+    assert np.array_equal(dc.ctx_lens.cpu().numpy(), nl)
+    assert np.array_equal(_bits(dc.k_pages, "bf16").view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_bits(dc.v_pages, "bf16").view(np.uint8), vp.view(np.uint8))
+
+
 def test_kv_append_skips_sequence_without_pages():
     import two_tower_attention_amd as tt
     rng = np.random.Generator(np.random.PCG64(3))
