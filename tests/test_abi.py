@@ -200,6 +200,8 @@ LMHEAD_BAD = [
     ("vocab0", dict(V=0), -2),
     ("remaining0", dict(rem=0, k=None), -2),
     ("flags", dict(flags=2), -4),
+    # 256 row tiles x 2^23 vocabulary tiles: 2^31 work-groups, one too many
+    ("grid_too_large", dict(B=4095, S=16, V=2**31 - 1), -2),
 ]
 
 
