@@ -86,24 +86,34 @@ struct LmParams {
 // step t and row block rb, one 1 KiB fragment whose lane l = 32*hl + ln holds
 // x[256*rt + 64*w + 32*rb + ln][64*s + 16*t + 8*hl .. +7], zero past R and
 // past H.  Fragment index ((((rt*4 + w)*nst + s)*kSteps + t)*2 + rb).
+// One work-group per (64-row group f = rt*4 + w, stage s): it reads the
+// group's 64 rows x 128 bytes with whole-row loads, transposes them through
+// LDS and writes the stage's 8 fragments (8 KiB) contiguously.
 __global__ __launch_bounds__(256) void lmhead_pack_kernel(const __bf16 *__restrict__ x,
                                                           bf16x8 *__restrict__ xp, int R, int H,
-                                                          int nst, long long n16) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // 16-byte unit
-  if (i >= n16) return;
-  const int lane = (int)(i & 63);
-  long long f = i >> 6;
-  const int rb = (int)(f & 1);
-  f >>= 1;
-  const int t = (int)(f % kSteps);
-  f /= kSteps;
-  const int s = (int)(f % nst);
-  f /= nst;
-  const long long row = f * kWR + 32 * rb + (lane & 31);  // f = rt*4 + w
-  const int k = s * kKS + 16 * t + 8 * (lane >> 5);
-  bf16x8 v = {};
-  if (row < R && k < H) v = *(const bf16x8 *)(x + row * H + k);
-  xp[i] = v;
+                                                          int nst) {
+  __shared__ bf16x8 tile[kWR][kKS / 8 + 1];  // [row][16-byte chunk], padded against bank conflicts
+  const int s = blockIdx.x % nst;
+  const long long f = blockIdx.x / nst;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = tid / 4, c = 2 * (tid % 4) + u;
+    const long long gr = f * kWR + row;
+    const int k = s * kKS + 8 * c;
+    bf16x8 v = {};
+    if (gr < R && k < H) v = *(const bf16x8 *)(x + gr * H + k);
+    tile[row][c] = v;
+  }
+  __syncthreads();
+  bf16x8 *dst = xp + ((size_t)f * nst + s) * (kSteps * 2 * 64);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;       // 16-byte unit of the stage: fragment e / 64, lane e % 64
+    const int frag = e >> 6, lane = e & 63;
+    const int t = frag >> 1, rb = frag & 1;
+    dst[e] = tile[32 * rb + (lane & 31)][2 * t + (lane >> 5)];
+  }
 }
 
 // lgkmcnt(0) only (gfx9 encoding): completes this wave's LDS reads.
@@ -364,9 +374,9 @@ hipError_t launch_lmhead_parts(const void *hidden, const void *weight, int R, in
     attr_done = true;
   }
   const int nst = (H + kKS - 1) / kKS;
-  const long long n16 = (long long)(lmhead_pack_bytes(R, H) / 16);
-  hipLaunchKernelGGL(lmhead_pack_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream,
-                     (const __bf16 *)hidden, (bf16x8 *)xpack, R, H, nst, n16);
+  const long long groups = (long long)((R + kRT - 1) / kRT) * 4 * nst;  // (64-row group, stage) pairs
+  hipLaunchKernelGGL(lmhead_pack_kernel, dim3((unsigned)groups), dim3(256), 0, stream,
+                     (const __bf16 *)hidden, (bf16x8 *)xpack, R, H, nst);
   LmParams prm;
   prm.xp = (const __bf16 *)xpack;
   prm.w = (const __bf16 *)weight;

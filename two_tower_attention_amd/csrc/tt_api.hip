@@ -277,12 +277,11 @@ static int check_lmhead_shape(int32_t B, int32_t S, int32_t V, int32_t H) {
   if (st) return st;
   if (H < 32 || H > 65536 || H % 32 != 0)
     return fail(TT_ERR_SHAPE, "hidden size %d must be a multiple of 32 in [32, 65536]", H);
-  // grids: one work-group per 256 x 256 logits tile, and the packing kernel's
-  // 16-byte units in 256-thread groups, must each stay below 2^31
+  // grids: one work-group per 256 x 256 logits tile, and one packing
+  // work-group per (64-row group, 64-element stage), must each stay below 2^31
   const long long R = (long long)B * S;
   const long long row_tiles = (R + 255) / 256, vocab_tiles = ((long long)V + 255) / 256;
-  // the packed copy is row_tiles * 4 waves * ceil(H/64) stages * 8 KiB
-  const long long pack_groups = row_tiles * 4 * ((H + 63) / 64) * 8192 / 16 / 256;
+  const long long pack_groups = row_tiles * 4 * ((H + 63) / 64);
   if (row_tiles * vocab_tiles > INT32_MAX || pack_groups > INT32_MAX)
     return fail(TT_ERR_SHAPE, "batch*block %lld with vocab %d and hidden size %d is too large for one launch", R, V, H);
   return TT_OK;
