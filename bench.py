@@ -336,19 +336,44 @@ def main():
     else:
         block_s = float("nan")
 
-    # ---- attention alone, HIP events on the launch stream, rotating inputs
+    # ---- attention alone, HIP events on the launch stream, rotating inputs.
+    # The launches are replayed from a HIP graph (as in the timed loop), so the
+    # figure is kernel time plus the inter-kernel gaps, not host launch cost;
+    # the eagerly launched figure is reported beside it.
     stream = torch.cuda.current_stream()
     ctx.copy_(ctx0)
     for it in range(6):
         attn(it % T, it % NL)
     torch.cuda.synchronize()
+
+    def attn_loop():
+        for it in range(args.attn_iters):
+            attn((it // NL) % T, it % NL)
+
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record(stream)
-    for it in range(args.attn_iters):
-        attn((it // NL) % T, it % NL)
+    attn_loop()
     a1.record(stream)
     torch.cuda.synchronize()
-    attn_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
+    attn_eager_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
+    attn_s = attn_eager_s
+    if not args.no_graph and not args.only_attn:
+        agraph = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(stream)
+        with torch.cuda.stream(s_cap):
+            with torch.cuda.graph(agraph, stream=s_cap):
+                attn_loop()
+        stream.wait_stream(s_cap)
+        agraph.replay()
+        torch.cuda.synchronize()
+        a0.record(stream)
+        agraph.replay()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        attn_s = a0.elapsed_time(a1) / 1e3 / args.attn_iters
+        del agraph
+    log("attention: eager %.1f us/launch, graph replay %.1f us/launch" % (attn_eager_s * 1e6, attn_s * 1e6))
     # the context tower's causal chunk ingest on the same inputs
     chunk_s = None
     if extras:
@@ -528,7 +553,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "tt_block_attn (split + combine launches)",
-                     "us_per_launch": attn_s * 1e6, "alg_bytes_per_launch": attn_bytes,
+                     "us_per_launch": attn_s * 1e6, "us_per_launch_eager": attn_eager_s * 1e6,
+                     "alg_bytes_per_launch": attn_bytes,
                      "tflops": attn_tfs, "mfma_frac": attn_tfs / MFMA_BF16_PEAK_TFLOPS},
         "cpu_baseline": cpu,
         "unmask": {"us_per_call": un_s * 1e6, "GB/s": un_gbs, "frac_hbm": un_gbs / HBM_PEAK_GBS},
