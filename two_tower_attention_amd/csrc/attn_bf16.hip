@@ -719,11 +719,13 @@ __device__ __forceinline__ unsigned char *begin_tile(const Unit &u, int i, int c
 
 // Context tiles [i0, ctx_end) of unit u through the LDS ring, in sub-ranges
 // whose pages fit the page-id cache.  LAG selects the wave-group role.
+// An idle wave (no valid query row) keeps the ring's barriers and issues its
+// share of the loads but computes nothing.
 template <int D, bool BIG, bool LAG>
 __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, int i0, int ctx_end,
                                               unsigned char *ring, int *pcache,
                                               const bf16x8 (&qr)[Geo<D>::KS], Acc<D> &A,
-                                              PTile<D> &P) {
+                                              PTile<D> &P, bool idle) {
   using G = Geo<D>;
   constexpr int kAhead = kStages - 2;  // tiles prefetched beyond the current one
   const int sub = max(1, (kPageCache * p.page_size) / kTile - 1);
@@ -756,7 +758,12 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
                                ring + ((i - c0 + kAhead) % kStages) * G::STAGE_BYTES, pg, pcache,
                                pbase, c1};
     };
-    if (!LAG) {
+    if (idle) {
+      for (int i = c0; i < c1; ++i) {
+        begin_tile<D>(u, i, c0, c1, ring, nvalid);
+        loads(i).issue();
+      }
+    } else if (!LAG) {
       for (int i = c0; i < c1; ++i) {
         const unsigned char *stage = begin_tile<D>(u, i, c0, c1, ring, nvalid);
         tile_lead<D>(p, stage, nvalid, nvalid < kTile, qr, A, P, loads(i));
@@ -822,8 +829,11 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
   // ---- context tiles [i0, ctx_end): one loop instance per role, so that the
   // register allocation of each is independent (same barrier sequence)
   const int ctx_end = min(i1, u.nreal - 1);
-  if (lag) context_tiles<D, BIG, true>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
-  else context_tiles<D, BIG, false>(p, u, i0, ctx_end, ring, pcache, qr, A, P);
+  // a wave whose 32 query rows all lie past S*g (block sizes with S*g not a
+  // multiple of 256) skips the compute
+  const bool idle = u.qc * kQRows + wave * 32 >= M;
+  if (lag) context_tiles<D, BIG, true>(p, u, i0, ctx_end, ring, pcache, qr, A, P, idle);
+  else context_tiles<D, BIG, false>(p, u, i0, ctx_end, ring, pcache, qr, A, P, idle);
   // ---- the block's own S keys/values (the unit's last real tile)
   if (i0 < u.nreal && i1 >= u.nreal) {
     unsigned char *stage = ring;
@@ -832,7 +842,7 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
     // chunk ingest: the lane's query row (block position t) sees keys 0..t
     const int qt = (u.qc * kQRows + wave * 32 + ln) / p.g;
     const int klim = p.causal ? min(p.S, qt + 1) : p.S;
-    tile_lead<D>(p, stage, klim, p.causal || p.S < kTile, qr, A, P, NoLoads{});
+    if (!idle) tile_lead<D>(p, stage, klim, p.causal || p.S < kTile, qr, A, P, NoLoads{});
     lds_barrier();
   }
 
@@ -855,7 +865,7 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
           *(bf16x4 *)(dst + 32 * db + 8 * r4 + 4 * hl) = __builtin_convertvector(v, bf16x4);
         }
     }
-  } else {
+  } else if (!idle) {  // the combine reads no row of an idle wave
     // partial O^T / l in bf16, accumulator layout: 4 x bf16 (registers
     // 4*r4 .. 4*r4+3) of lane l at (((wave*DB + db)*4 + r4)*64 + l); features
     // 32*db + 8*r4 + 4*(l/32) + 0..3 of query row 32*wave + l%32.
