@@ -73,6 +73,23 @@ struct Acc {
   }
 };
 
+// Merges the partials parts[first], parts[first + stride], ... below `end`
+// into a, eight loads in flight at a time (the merge does not depend on the
+// order: max, lowest index among equal maxima, rescaled sums).
+__device__ __forceinline__ void merge_parts(Acc &a, const Part *parts, int first, int end,
+                                            int stride) {
+  constexpr int U = 8;
+  for (int c0 = first; c0 < end; c0 += U * stride) {
+    Part pt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u * stride < end) pt[u] = parts[c0 + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u * stride < end) a.merge(pt[u].m, pt[u].s, pt[u].idx);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void unmask_rowreduce_kernel(const float *logits, int V,
                                                                     int chunk_len, int chunks,
                                                                     int vec, Part *parts) {
@@ -135,10 +152,7 @@ __global__ __launch_bounds__(64) void unmask_commit_kernel(const Part *parts, in
   if (t < S) {
     Acc a;
     a.init();
-    for (int k = 0; k < chunks; ++k) {
-      const Part pt = parts[r * chunks + k];
-      a.merge(pt.m, pt.s, pt.idx);
-    }
+    merge_parts(a, parts + r * chunks, 0, chunks, 1);
     c = 1.f / a.s;
     id = a.idx == INT_MAX ? 0 : a.idx;
     mk = mask[r] != 0;
@@ -177,10 +191,7 @@ __global__ __launch_bounds__(64) void unmask_threshold_commit_kernel(
   if (t < S) {
     Acc a;
     a.init();
-    for (int k = 0; k < chunks; ++k) {
-      const Part pt = parts[r * chunks + k];
-      a.merge(pt.m, pt.s, pt.idx);
-    }
+    merge_parts(a, parts + r * chunks, 0, chunks, 1);
     c = 1.f / a.s;
     id = a.idx == INT_MAX ? 0 : a.idx;
     mk = mask[r] != 0;
@@ -219,10 +230,7 @@ __global__ __launch_bounds__(64) void unmask_merge_kernel(const Part *parts, int
   const int r = blockIdx.x, lane = threadIdx.x;
   Acc a;
   a.init();
-  for (int c = lane; c < chunks; c += 64) {
-    const Part pt = parts[(size_t)r * chunks + c];
-    a.merge(pt.m, pt.s, pt.idx);
-  }
+  merge_parts(a, parts + (size_t)r * chunks, lane, chunks, 64);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float m2 = __shfl_xor(a.m, o, 64);
