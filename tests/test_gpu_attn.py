@@ -78,6 +78,10 @@ EDGE = [
     ("odd_block", 3, 5, 6, 3, 64, [17, 0, 90], 16),
     ("many_units", 100, 16, 32, 2, 128, list(range(0, 1000, 10)), 256),
     ("long_split", 1, 16, 32, 2, 128, [20000], 256),
+    # S*g = 160: waves 0-4 hold rows (lag wave 4 among them), waves 5-7 are idle
+    ("lag_partly_idle", 2, 10, 32, 2, 128, [100, 3000], 256),
+    # S*g = 384: the second query chunk holds 128 rows, its waves 4-7 are idle
+    ("second_chunk_half_full", 2, 24, 32, 2, 128, [90, 2000], 256),
 ]
 
 
