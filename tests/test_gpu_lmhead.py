@@ -83,6 +83,8 @@ CASES = [
     ("rows_over_one_tile", 20, 16, 128, 1024),  # 320 rows: two row tiles, the second ragged
     ("one_row", 1, 1, 128, 513),
     ("h512", 2, 16, 512, 4096),
+    ("hidden_max", 1, 16, 65536, 512),           # 1024 stages per tile
+    ("hidden_odd_stages", 2, 3, 4064, 700),      # 63.5 stages: a half last stage, padded to an even count
 ]
 
 
