@@ -1034,15 +1034,12 @@ template <int D, bool BIG>
 hipError_t launch_split(const Params &prm, hipStream_t stream) {
   const size_t pre_bytes = (size_t)(2 * prm.B + 1) * sizeof(int);   // pre[] and lens[]
   const size_t split_lds = Geo<D>::RING_BYTES + kPageCache * sizeof(int) + pre_bytes;
-  static bool attr_done = false;   // benign race: every caller sets the same value
-  if (!attr_done) {
-    const hipError_t e = hipFuncSetAttribute((const void *)attn_split_kernel<D, BIG>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(Geo<D>::RING_BYTES + kPageCache * sizeof(int) +
-                                                   (2 * kMaxBatch + 1) * sizeof(int)));
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<unsigned long long> attr_done{0};  // per device
+  const hipError_t e = lds_limit_once((const void *)attn_split_kernel<D, BIG>,
+                                      (int)(Geo<D>::RING_BYTES + kPageCache * sizeof(int) +
+                                            (2 * kMaxBatch + 1) * sizeof(int)),
+                                      attr_done);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_split_kernel<D, BIG>), dim3(prm.G), dim3(kThreads), split_lds, stream, prm);
   return hipGetLastError();
 }

@@ -365,14 +365,9 @@ size_t lmhead_pack_bytes(int R, int H) {
 
 hipError_t launch_lmhead_parts(const void *hidden, const void *weight, int R, int H, int V,
                                UnmaskPart *parts, void *xpack, hipStream_t stream) {
-  static bool attr_done = false;  // benign race: every caller sets the same value
-  if (!attr_done) {
-    const hipError_t e = hipFuncSetAttribute((const void *)lmhead_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             kSlots * kStageBytes);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<unsigned long long> attr_done{0};  // per device
+  const hipError_t e = lds_limit_once((const void *)lmhead_kernel, kSlots * kStageBytes, attr_done);
+  if (e != hipSuccess) return e;
   const int nst = (H + kKS - 1) / kKS;
   const long long groups = (long long)((R + kRT - 1) / kRT) * 4 * nst;  // (64-row group, stage) pairs
   hipLaunchKernelGGL(lmhead_pack_kernel, dim3((unsigned)groups), dim3(256), 0, stream,

@@ -5,9 +5,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tt.h"
 
 namespace tt {
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device: the attribute is per device, and `done` keeps one bit per
+// device id below 64 (higher ids set it on every call).  Concurrent first
+// calls may both set it, which is harmless.
+inline hipError_t lds_limit_once(const void *kernel, int bytes, std::atomic<unsigned long long> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
