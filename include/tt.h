@@ -26,6 +26,11 @@
  *     all backed by valid pages.
  *   - Calls are stateless apart from a per-thread error string; concurrent
  *     calls on different streams must not share a workspace.
+ *   - Results are bitwise reproducible for the same inputs and shapes (fixed
+ *     reduction orders, no atomics on data).  The calls allocate nothing and
+ *     enqueue only kernel launches, so they can be captured in a HIP graph
+ *     and replayed; the first call on each device also sets a kernel
+ *     attribute, so make one call before capturing.
  */
 #ifndef TT_H
 #define TT_H
