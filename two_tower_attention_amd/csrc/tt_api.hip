@@ -289,15 +289,12 @@ static int check_lmhead_shape(int32_t B, int32_t S, int32_t V, int32_t H) {
 
 static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// parts [R, chunks], the merged row partials [R], then the hidden state in
-// MFMA fragment order
+// parts [R, chunks], then the hidden state in MFMA fragment order
 static size_t lmhead_parts_bytes(int32_t B, int32_t S, int32_t V) {
   return round256((size_t)B * S * tt::lmhead_chunks(V) * sizeof(tt::UnmaskPart));
 }
 static size_t lmhead_ws_bytes(int32_t B, int32_t S, int32_t V, int32_t H) {
-  const size_t R = (size_t)B * S;
-  return lmhead_parts_bytes(B, S, V) + round256(R * sizeof(tt::UnmaskPart)) +
-         round256(tt::lmhead_pack_bytes((int)R, H));
+  return lmhead_parts_bytes(B, S, V) + round256(tt::lmhead_pack_bytes(B * S, H));
 }
 
 int tt_lmhead_unmask_workspace_bytes(int32_t B, int32_t S, int32_t V, int32_t H, size_t *bytes) {
@@ -308,11 +305,12 @@ int tt_lmhead_unmask_workspace_bytes(int32_t B, int32_t S, int32_t V, int32_t H,
   return ok();
 }
 
-// Validation and the fused head + row reduction shared by the two commit forms;
-// on success *merged points at the [B*S] row partials in the workspace.
+// Validation and the fused head + tile reduction shared by the two commit
+// forms; on success *parts points at the [B*S, lmhead_chunks(V)] partials in
+// the workspace, which the commit kernels merge per row.
 static int lmhead_rows(const void *hidden, const void *weight, int32_t B, int32_t S, int32_t V,
                        int32_t H, void *workspace, size_t workspace_bytes, hipStream_t s,
-                       tt::UnmaskPart **merged) {
+                       tt::UnmaskPart **parts) {
   if (!hidden || !weight) return fail(TT_ERR_NULL, "hidden and weight are required");
   if (!aligned(hidden, 16) || !aligned(weight, 16))
     return fail(TT_ERR_UNSUPPORTED, "hidden and weight must be 16-byte aligned");
@@ -323,12 +321,9 @@ static int lmhead_rows(const void *hidden, const void *weight, int32_t B, int32_
   if (!aligned(workspace, 16)) return fail(TT_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (device_cus(nullptr) <= 0) return fail(TT_ERR_NO_DEVICE, "no HIP device");
   const int R = B * S;
-  tt::UnmaskPart *parts = (tt::UnmaskPart *)workspace;
-  *merged = (tt::UnmaskPart *)((unsigned char *)workspace + lmhead_parts_bytes(B, S, V));
-  void *xpack = (unsigned char *)workspace + lmhead_parts_bytes(B, S, V) +
-                round256((size_t)R * sizeof(tt::UnmaskPart));
-  hipError_t e = tt::launch_lmhead_parts(hidden, weight, R, H, V, parts, xpack, s);
-  if (e == hipSuccess) e = tt::launch_unmask_merge(parts, tt::lmhead_chunks(V), R, *merged, s);
+  *parts = (tt::UnmaskPart *)workspace;
+  void *xpack = (unsigned char *)workspace + lmhead_parts_bytes(B, S, V);
+  const hipError_t e = tt::launch_lmhead_parts(hidden, weight, R, H, V, *parts, xpack, s);
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return TT_OK;
 }
@@ -348,11 +343,11 @@ int tt_lmhead_unmask(const void *hidden, const void *weight, uint8_t *mask,
   if (!aligned(ids_out, 4) || (k_commit && !aligned(k_commit, 4)) || (conf_out && !aligned(conf_out, 4)))
     return fail(TT_ERR_UNSUPPORTED, "ids_out, k_commit, conf_out must be 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  tt::UnmaskPart *merged = nullptr;
-  st = lmhead_rows(hidden, weight, B, S, V, H, workspace, workspace_bytes, s, &merged);
+  tt::UnmaskPart *parts = nullptr;
+  st = lmhead_rows(hidden, weight, B, S, V, H, workspace, workspace_bytes, s, &parts);
   if (st) return st;
-  const hipError_t e = tt::launch_unmask_commit(merged, 1, B, S, mask, k_commit, remaining_steps,
-                                                ids_out, commit_out, conf_out, flags, s);
+  const hipError_t e = tt::launch_unmask_commit(parts, tt::lmhead_chunks(V), B, S, mask, k_commit,
+                                                remaining_steps, ids_out, commit_out, conf_out, flags, s);
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -372,11 +367,11 @@ int tt_lmhead_unmask_threshold(const void *hidden, const void *weight, uint8_t *
   if (!aligned(ids_out, 4) || (nsteps && !aligned(nsteps, 4)) || (conf_out && !aligned(conf_out, 4)))
     return fail(TT_ERR_UNSUPPORTED, "ids_out, nsteps, conf_out must be 4-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  tt::UnmaskPart *merged = nullptr;
-  st = lmhead_rows(hidden, weight, B, S, V, H, workspace, workspace_bytes, s, &merged);
+  tt::UnmaskPart *parts = nullptr;
+  st = lmhead_rows(hidden, weight, B, S, V, H, workspace, workspace_bytes, s, &parts);
   if (st) return st;
-  const hipError_t e = tt::launch_unmask_threshold_commit(merged, 1, B, S, mask, gamma, ids_out,
-                                                          commit_out, conf_out, nsteps, flags, s);
+  const hipError_t e = tt::launch_unmask_threshold_commit(parts, tt::lmhead_chunks(V), B, S, mask, gamma,
+                                                          ids_out, commit_out, conf_out, nsteps, flags, s);
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -91,10 +91,6 @@ hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uin
                                    int32_t *nsteps, uint32_t flags, void *workspace,
                                    hipStream_t stream);
 
-// Merges `chunks` partials per row of parts [rows, chunks] into out [rows].
-hipError_t launch_unmask_merge(const UnmaskPart *parts, int chunks, int rows, UnmaskPart *out,
-                               hipStream_t stream);
-
 // The commit stage of tt_unmask / tt_unmask_threshold on row partials
 // [B*S, chunks].
 hipError_t launch_unmask_commit(const UnmaskPart *parts, int chunks, int B, int S, uint8_t *mask,

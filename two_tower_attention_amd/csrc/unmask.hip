@@ -138,28 +138,70 @@ __global__ __launch_bounds__(kThreads) void unmask_rowreduce_kernel(const float 
   }
 }
 
-__global__ __launch_bounds__(64) void unmask_commit_kernel(const Part *parts, int chunks, int S,
-                                                           uint8_t *mask, const int32_t *k_commit,
-                                                           int remaining, int32_t *ids,
-                                                           uint8_t *commit, float *conf,
-                                                           uint32_t flags) {
-  __shared__ float cs[64];
-  __shared__ int ms[64];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const size_t r = (size_t)b * S + t;
-  float c = 0.f;
-  int id = 0, mk = 0;
-  if (t < S) {
+// Commit kernels: one work-group per sequence.  First the chunk partials of
+// each row are merged into the row's confidence and id in LDS; then the first
+// wave ranks the sequence's masked slots.  With few chunks per row (a
+// one-wave work-group) lane t merges row t's chunks itself; with many (the
+// fused LM head's 256-entry tiles) each wave takes rows wave, wave + waves,
+// ..., its lane j chunks j, j + 64, ..., then a wave reduction.
+constexpr int kCommitWaves = 16;
+constexpr int kLanePerRowChunks = 8;  // at most this many chunks: lane per row
+
+__device__ __forceinline__ void merge_rows(const Part *parts, int chunks, int S, const uint8_t *mask,
+                                           float *cs, int *is, int *ms) {
+  const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int waves = blockDim.x >> 6;
+  if (threadIdx.x < 64 && threadIdx.x >= S) {  // slots past the block take no part
+    cs[threadIdx.x] = 0.f;
+    is[threadIdx.x] = 0;
+    ms[threadIdx.x] = 0;
+  }
+  if (waves == 1) {
+    const int t = lane;
+    if (t < S) {
+      const size_t r = (size_t)b * S + t;
+      Acc a;
+      a.init();
+      merge_parts(a, parts + r * chunks, 0, chunks, 1);
+      cs[t] = 1.f / a.s;
+      is[t] = a.idx == INT_MAX ? 0 : a.idx;
+      ms[t] = mask[r] != 0;
+    }
+    __syncthreads();
+    return;
+  }
+  for (int t = wave; t < S; t += waves) {
+    const size_t r = (size_t)b * S + t;
     Acc a;
     a.init();
-    merge_parts(a, parts + r * chunks, 0, chunks, 1);
-    c = 1.f / a.s;
-    id = a.idx == INT_MAX ? 0 : a.idx;
-    mk = mask[r] != 0;
+    merge_parts(a, parts + r * chunks, lane, chunks, 64);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(a.m, o, 64);
+      const float s2 = __shfl_xor(a.s, o, 64);
+      const int i2 = __shfl_xor(a.idx, o, 64);
+      a.merge(m2, s2, i2);
+    }
+    if (lane == 0) {
+      cs[t] = 1.f / a.s;
+      is[t] = a.idx == INT_MAX ? 0 : a.idx;
+      ms[t] = mask[r] != 0;
+    }
   }
-  cs[t] = c;
-  ms[t] = mk;
   __syncthreads();
+}
+
+__global__ __launch_bounds__(64 * kCommitWaves) void unmask_commit_kernel(
+    const Part *parts, int chunks, int S, uint8_t *mask, const int32_t *k_commit, int remaining,
+    int32_t *ids, uint8_t *commit, float *conf, uint32_t flags) {
+  __shared__ float cs[64];
+  __shared__ int is[64], ms[64];
+  merge_rows(parts, chunks, S, mask, cs, is, ms);
+  if (threadIdx.x >= 64) return;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const size_t r = (size_t)b * S + t;
+  const float c = cs[t];
+  const int mk = ms[t];
   int n = 0;
   for (int u = 0; u < S; ++u) n += ms[u];
   int kb = k_commit ? k_commit[b] : (n + remaining - 1) / remaining;
@@ -169,7 +211,7 @@ __global__ __launch_bounds__(64) void unmask_commit_kernel(const Part *parts, in
     for (int u = 0; u < S; ++u)
       rank += (ms[u] && (cs[u] > c || (cs[u] == c && u < t))) ? 1 : 0;
     const int com = (mk && rank < kb) ? 1 : 0;
-    ids[r] = id;
+    ids[r] = is[t];
     commit[r] = (uint8_t)com;
     if (conf) conf[r] = c;
     if ((flags & TT_UNMASK_UPDATE_MASK) && com) mask[r] = 0;
@@ -177,28 +219,18 @@ __global__ __launch_bounds__(64) void unmask_commit_kernel(const Part *parts, in
 }
 
 // Threshold form: every masked slot with conf > gamma commits; if none does,
-// the masked slot ranked first by (conf desc, slot asc) does.  One wave per
-// sequence, as the count form.
-__global__ __launch_bounds__(64) void unmask_threshold_commit_kernel(
+// the masked slot ranked first by (conf desc, slot asc) does.
+__global__ __launch_bounds__(64 * kCommitWaves) void unmask_threshold_commit_kernel(
     const Part *parts, int chunks, int S, uint8_t *mask, float gamma, int32_t *ids,
     uint8_t *commit, float *conf, int32_t *nsteps, uint32_t flags) {
   __shared__ float cs[64];
-  __shared__ int ms[64];
+  __shared__ int is[64], ms[64];
+  merge_rows(parts, chunks, S, mask, cs, is, ms);
+  if (threadIdx.x >= 64) return;
   const int b = blockIdx.x, t = threadIdx.x;
   const size_t r = (size_t)b * S + t;
-  float c = 0.f;
-  int id = 0, mk = 0;
-  if (t < S) {
-    Acc a;
-    a.init();
-    merge_parts(a, parts + r * chunks, 0, chunks, 1);
-    c = 1.f / a.s;
-    id = a.idx == INT_MAX ? 0 : a.idx;
-    mk = mask[r] != 0;
-  }
-  cs[t] = c;
-  ms[t] = mk;
-  __syncthreads();
+  const float c = cs[t];
+  const int mk = ms[t];
   int n = 0, n_above = 0;
   for (int u = 0; u < S; ++u) {
     n += ms[u];
@@ -214,7 +246,7 @@ __global__ __launch_bounds__(64) void unmask_threshold_commit_kernel(
         rank += (ms[u] && (cs[u] > c || (cs[u] == c && u < t))) ? 1 : 0;
       com = (mk && rank == 0) ? 1 : 0;
     }
-    ids[r] = id;
+    ids[r] = is[t];
     commit[r] = (uint8_t)com;
     if (conf) conf[r] = c;
     if ((flags & TT_UNMASK_UPDATE_MASK) && com) mask[r] = 0;
@@ -222,42 +254,19 @@ __global__ __launch_bounds__(64) void unmask_threshold_commit_kernel(
   if (t == 0 && nsteps && n > 0) nsteps[b] += 1;
 }
 
-// One wave per row: lane j merges chunks j, j + 64, ...; then a wave
-// reduction.  The merge keeps the lower index on equal maxima, so the order
-// of chunks does not matter.
-__global__ __launch_bounds__(64) void unmask_merge_kernel(const Part *parts, int chunks,
-                                                          Part *out) {
-  const int r = blockIdx.x, lane = threadIdx.x;
-  Acc a;
-  a.init();
-  merge_parts(a, parts + (size_t)r * chunks, lane, chunks, 64);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(a.m, o, 64);
-    const float s2 = __shfl_xor(a.s, o, 64);
-    const int i2 = __shfl_xor(a.idx, o, 64);
-    a.merge(m2, s2, i2);
-  }
-  if (lane == 0) {
-    Part pt;
-    pt.m = a.m; pt.s = a.s; pt.idx = a.idx; pt.pad = 0;
-    out[r] = pt;
-  }
-}
-
 }  // namespace
 
-hipError_t launch_unmask_merge(const UnmaskPart *parts, int chunks, int rows, UnmaskPart *out,
-                               hipStream_t stream) {
-  hipLaunchKernelGGL(unmask_merge_kernel, dim3(rows), dim3(64), 0, stream, parts, chunks, out);
-  return hipGetLastError();
+// threads of a commit work-group: one wave when rows have few chunks, else a
+// wave per row (up to kCommitWaves)
+static int commit_threads(int chunks, int S) {
+  return chunks <= kLanePerRowChunks ? 64 : 64 * (S < kCommitWaves ? S : kCommitWaves);
 }
 
 hipError_t launch_unmask_commit(const UnmaskPart *parts, int chunks, int B, int S, uint8_t *mask,
                                 const int32_t *k_commit, int remaining_steps, int32_t *ids,
                                 uint8_t *commit, float *conf, uint32_t flags, hipStream_t stream) {
-  hipLaunchKernelGGL(unmask_commit_kernel, dim3(B), dim3(64), 0, stream, parts, chunks, S, mask,
-                     k_commit, remaining_steps, ids, commit, conf, flags);
+  hipLaunchKernelGGL(unmask_commit_kernel, dim3(B), dim3(commit_threads(chunks, S)), 0, stream, parts,
+                     chunks, S, mask, k_commit, remaining_steps, ids, commit, conf, flags);
   return hipGetLastError();
 }
 
@@ -265,8 +274,8 @@ hipError_t launch_unmask_threshold_commit(const UnmaskPart *parts, int chunks, i
                                           uint8_t *mask, float gamma, int32_t *ids,
                                           uint8_t *commit, float *conf, int32_t *nsteps,
                                           uint32_t flags, hipStream_t stream) {
-  hipLaunchKernelGGL(unmask_threshold_commit_kernel, dim3(B), dim3(64), 0, stream, parts, chunks,
-                     S, mask, gamma, ids, commit, conf, nsteps, flags);
+  hipLaunchKernelGGL(unmask_threshold_commit_kernel, dim3(B), dim3(commit_threads(chunks, S)), 0,
+                     stream, parts, chunks, S, mask, gamma, ids, commit, conf, nsteps, flags);
   return hipGetLastError();
 }
 
