@@ -253,9 +253,9 @@ int tt_unmask_threshold(const float *logits, uint8_t *mask, float gamma, int32_t
  * largest logits of a row are that close, commits where confidences are.
  * Workspace: tt_lmhead_unmask_workspace_bytes (16-byte aligned, caller-owned,
  * needed for batch > 0).  It holds one 16-byte partial per row and 256-entry
- * vocabulary tile, one merged record per row, and a copy of the hidden state
- * rearranged for the matrix cores (about B*S*H*2 bytes, rows rounded up to
- * 256); its contents on entry do not matter.  Errors as tt_unmask;
+ * vocabulary tile and a copy of the hidden state rearranged for the matrix
+ * cores (about B*S*H*2 bytes, rows rounded up to 256); its contents on entry
+ * do not matter.  Errors as tt_unmask;
  * TT_ERR_SHAPE for H.
  */
 int tt_lmhead_unmask_workspace_bytes(int32_t batch, int32_t block, int32_t vocab,
