@@ -95,10 +95,11 @@ def assert_attn_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = 
     return max_abs, rel
 
 
-def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff, tie=COMMIT_TIE):
+def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff, tie=COMMIT_TIE, rel=False):
     """Commit comparator: exact count, only masked slots, and any difference
-    from the oracle's set only among near-ties (within ``tie``) of the k-th
-    confidence."""
+    from the oracle's set only among near-ties of the k-th confidence c*:
+    |conf - c*| <= tie, or <= tie * c* with ``rel`` (for confidences computed
+    from logits that carry a rounding error, whose effect on 1/Z is relative)."""
     B, S = mask.shape
     for b in range(B):
         cg, cr = commit_gpu[b].astype(bool), commit_ref[b].astype(bool)
@@ -109,18 +110,20 @@ def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff, tie=COMMIT_T
         if diff.size:
             masked_conf = np.sort(conf_ref[b][m])[::-1]
             cstar = masked_conf[k_eff[b] - 1]
-            assert np.all(np.abs(conf_ref[b][diff] - cstar) <= tie), \
-                (b, diff, conf_ref[b][diff], cstar)
+            band = tie * cstar if rel else tie
+            assert np.all(np.abs(conf_ref[b][diff] - cstar) <= band), \
+                (b, diff, conf_ref[b][diff], cstar, band)
 
 
-def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma, tie=COMMIT_TIE):
+def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma, tie=COMMIT_TIE, rel=False):
     """Threshold-rule comparator.  The GPU decides conf > gamma on its fp32
     confidence, the oracle's confidence is fp64, so a slot whose oracle
     confidence lies within COMMIT_TIE of gamma may go either way; the same band
     applies to ties of the fallback's maximum.  Everything else is fixed:
     only masked slots commit; slots surely above gamma commit, slots surely
     below it do not (unless a fallback); a fallback commits exactly one slot
-    among the most confident."""
+    among the most confident.  With ``rel`` the band is ``tie`` times the
+    confidence it is taken around (gamma, or the fallback's maximum)."""
     B, S = mask.shape
     for b in range(B):
         cg = commit_gpu[b].astype(bool)
@@ -130,8 +133,9 @@ def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma, tie=COMMIT_TIE
         if not m.any():
             assert not cg.any()
             continue
-        sure = m & (c > gamma + tie)
-        near = m & (np.abs(c - gamma) <= tie)
+        gband = tie * abs(gamma) if rel else tie
+        sure = m & (c > gamma + gband)
+        near = m & (np.abs(c - gamma) <= gband)
         if sure.any():
             assert np.all(cg[sure]), (b, "a slot surely above gamma was not committed")
             assert not np.any(cg & m & ~sure & ~near), (b, "a slot surely below gamma committed")
@@ -141,5 +145,6 @@ def assert_threshold_commit_ok(commit_gpu, conf_ref, mask, gamma, tie=COMMIT_TIE
         # commits one slot whose confidence is within the band of the maximum)
         assert cg.any(), (b, "no progress")
         judged_above = np.all(near[cg])
-        fallback = cg.sum() == 1 and abs(c[cg][0] - c[m].max()) <= tie
+        mband = tie * c[m].max() if rel else tie
+        fallback = cg.sum() == 1 and abs(c[cg][0] - c[m].max()) <= mband
         assert judged_above or fallback, (b, np.nonzero(cg)[0], c[cg], c[m].max())

@@ -127,6 +127,23 @@ def test_workspace_sizes(lib):
     assert n.value >= 32 * 16 * 16
 
 
+def test_tile_count_beyond_device_index(lib):
+    """The device plans with int tile indices: a shape whose flat tile list
+    could exceed that range is rejected on the host (TT_ERR_SHAPE) by both the
+    workspace query and the call, before any device work."""
+    d = good_desc(B=2048, S=1, Hq=4096, Hkv=4096, D=64, page_size=4096, max_pages=256,
+                  num_pages=1 << 20, max_ctx_len=1 << 20)
+    n = ctypes.c_size_t(0)
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == -2
+    assert "tiles" in tt.tt_last_error()
+    st = lib.tt_block_attn(ctypes.byref(d), *([FAKE] * 8), FAKE, ctypes.c_size_t(1 << 40), None)
+    assert st in (-2, -6)           # no device here: the device query may come first
+    # just inside the bound: 2048 sequences x 16 KV heads x 16389 tiles < 2^31
+    ok = good_desc(B=2048, S=1, Hq=16, Hkv=16, D=64, page_size=4096, max_pages=256,
+                   num_pages=1 << 20, max_ctx_len=1 << 20)
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(ok), ctypes.byref(n)) == 0
+
+
 def test_workspace_too_small(lib):
     d = good_desc()
     st = lib.tt_block_attn(ctypes.byref(d), *([FAKE] * 8), FAKE, ctypes.c_size_t(16), None)

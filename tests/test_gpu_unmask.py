@@ -106,6 +106,9 @@ def test_commit_edge_counts():
     check(logits, mask, np.array([0, 4, 100, 1, -5, 16], np.int32))
     for rem in (1, 2, 5, 16, 1000):
         check(logits, mask, None, rem)
+    # ceil(#masked / remaining_steps) must not overflow near INT_MAX: one slot each
+    ids, com, _ = check(logits, mask, None, 2**31 - 1)
+    assert com.sum(axis=1).tolist() == [1, 0, 1, 1, 1, 1]
 
 
 def test_small_blocks():

@@ -728,7 +728,10 @@ __device__ __forceinline__ void context_tiles(const Params &p, const Unit &u, in
                                               PTile<D> &P, bool idle) {
   using G = Geo<D>;
   constexpr int kAhead = kStages - 2;  // tiles prefetched beyond the current one
-  const int sub = max(1, (kPageCache * p.page_size) / kTile - 1);
+  // A sub-range of `sub` tiles starting at any in-page offset o (o < page_size)
+  // spans floor((o + 64*sub - 1) / page_size) + 1 <= kPageCache pages when
+  // 64*sub <= (kPageCache - 1) * page_size, so its page ids fit the cache.
+  const int sub = max(1, ((kPageCache - 1) * p.page_size) / kTile);
   for (int c0 = i0; c0 < ctx_end; c0 += sub) {
     const int c1 = min(c0 + sub, ctx_end);
     const int pbase = (c0 * kTile) >> p.lps;
@@ -1070,8 +1073,10 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus) {
   p.qchunks = (p.S * p.g + kQRows - 1) / kQRows;
   const float scale = d.scale > 0.f ? d.scale : 1.0f / sqrtf((float)p.D);
   p.scale_log2 = scale * 1.4426950408889634f;
-  const long tiles = (long)p.B * p.Hkv * p.qchunks * ((p.max_ctx + kTile - 1) / kTile + 1 + kUnitPad);
-  long G = (tiles + kMinTiles - 1) / kMinTiles;
+  const long long tiles =
+      (long long)p.B * p.Hkv * p.qchunks * ((p.max_ctx + kTile - 1) / kTile + 1 + kUnitPad);
+  p.tiles = tiles;
+  long long G = (tiles + kMinTiles - 1) / kMinTiles;
   if (G > cus) G = cus;
   if (G > 1024) G = 1024;  // the combine keeps one slot id per contributor in LDS
   if (G < 1) G = 1;

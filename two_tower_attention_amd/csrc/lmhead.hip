@@ -8,7 +8,7 @@
 // (x the final hidden state [R, H], w the head [V, H], bf16; fp32
 // accumulation).  Here the logits never reach HBM: a work-group computes a
 // 256 (vocabulary) x 256 (rows) tile of logits^T on MFMA and reduces it on
-// the spot to, per row and 128-entry vocabulary chunk, the unmask's partial
+// the spot to, per row and 256-entry vocabulary chunk (one tile), the unmask's partial
 // (max, lowest index of the max, sum exp(l - max)); the unmask's merge and
 // commit kernels finish the rule.
 //

@@ -126,7 +126,11 @@ int tt_block_attn_workspace_bytes(const tt_attn_desc *d, size_t *bytes) {
     *bytes = 0;
     return ok();
   }
-  *bytes = tt::plan_bf16_attn(*d, planning_cus()).ws_bytes;
+  const tt::AttnPlan plan = tt::plan_bf16_attn(*d, planning_cus());
+  if (plan.tiles > tt::kMaxAttnTiles)
+    return fail(TT_ERR_SHAPE, "%lld key tiles exceed what one launch indexes (%lld)", plan.tiles,
+                tt::kMaxAttnTiles);
+  *bytes = plan.ws_bytes;
   return ok();
 }
 
@@ -153,6 +157,9 @@ static int block_attn(const tt_attn_desc *d, const void *q, const void *k_blk, c
   hipError_t e;
   if (d->dtype == TT_BF16) {
     const tt::AttnPlan plan = tt::plan_bf16_attn(*d, cus);
+    if (plan.tiles > tt::kMaxAttnTiles)
+      return fail(TT_ERR_SHAPE, "%lld key tiles exceed what one launch indexes (%lld)", plan.tiles,
+                  tt::kMaxAttnTiles);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
       return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
                   workspace ? workspace_bytes : (size_t)0);

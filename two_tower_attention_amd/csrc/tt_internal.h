@@ -43,7 +43,12 @@ struct AttnPlan {
   int G;             // work-groups in the split launch
   float scale_log2;  // softmax scale * log2(e)
   size_t ws_bytes;   // workspace bytes
+  long long tiles;   // upper bound on the flat tile count (the device indexes it in int)
 };
+
+// Largest flat tile count the device-side plan (int prefix sums and ranges)
+// can index with headroom for the work-group range arithmetic.
+constexpr long long kMaxAttnTiles = (1ll << 31) - (1ll << 20);
 
 // Plans a bf16 call for a device with `cus` compute units.
 AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus);
@@ -102,7 +107,7 @@ hipError_t launch_unmask_threshold_commit(const UnmaskPart *parts, int chunks, i
                                           uint32_t flags, hipStream_t stream);
 
 // LM head fused with the unmask's row reduction: hidden [R, H] and weight
-// [V, H] in bf16 -> per (row, 128-vocabulary chunk) partials [R, lmhead_chunks(V)].
+// [V, H] in bf16 -> per (row, 256-entry vocabulary tile) partials [R, lmhead_chunks(V)].
 // xpack: lmhead_pack_bytes(R, H) bytes of scratch (16-byte aligned) for the
 // hidden state in MFMA fragment order.
 int lmhead_chunks(int V);

@@ -204,7 +204,9 @@ __global__ __launch_bounds__(64 * kCommitWaves) void unmask_commit_kernel(
   const int mk = ms[t];
   int n = 0;
   for (int u = 0; u < S; ++u) n += ms[u];
-  int kb = k_commit ? k_commit[b] : (n + remaining - 1) / remaining;
+  // ceil(n / remaining) in 64 bits: n + remaining - 1 overflows int for
+  // remaining_steps near INT_MAX
+  int kb = k_commit ? k_commit[b] : (int)(((long long)n + remaining - 1) / remaining);
   kb = min(max(kb, 0), n);
   if (t < S) {
     int rank = 0;
