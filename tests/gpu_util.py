@@ -95,6 +95,26 @@ def assert_attn_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = 
     return max_abs, rel
 
 
+def assert_attn_units(got: np.ndarray, ref: np.ndarray, Hkv: int, dtype: str, what: str = ""):
+    """Whole-tensor bound, then the rel-L2 bound again on every (b, h_kv) unit
+    (its S x g query rows), so an error confined to one unit (a dropped or
+    doubled tile of one sequence) cannot hide in the aggregate.  Outputs are
+    [B, S, Hq, D] with query head h reading key/value head h // g."""
+    assert_attn_close(got, ref, dtype, what)
+    B, S, Hq, D = ref.shape
+    g = Hq // Hkv
+    lim_rel = ATTN_REL_L2 if dtype == "bf16" else F32_REL_L2
+    gu = got.reshape(B, S, Hkv, g, D)
+    ru = ref.reshape(B, S, Hkv, g, D)
+    num = np.sqrt(((gu - ru) ** 2).sum(axis=(1, 3, 4)))
+    den = np.maximum(np.sqrt((ru ** 2).sum(axis=(1, 3, 4))), 1e-300)
+    rel = num / den
+    worst = np.unravel_index(int(np.argmax(rel)), rel.shape)
+    assert rel.max() <= lim_rel, "%s unit (b=%d, h_kv=%d) rel_l2=%.3g (<= %.3g)" % (
+        what, worst[0], worst[1], rel.max(), lim_rel)
+    return float(rel.max())
+
+
 def assert_commit_ok(commit_gpu, commit_ref, conf_ref, mask, k_eff, tie=COMMIT_TIE, rel=False):
     """Commit comparator: exact count, only masked slots, and any difference
     from the oracle's set only among near-ties of the k-th confidence c*:

@@ -1,7 +1,7 @@
 """GPU parity of tt_block_attn against the fp64 oracle (through the C ABI).
 
-Small cases compare every output element; the full-size workloads compare
-sampled rows that the oracle computes one by one.  Outputs are pre-filled with
+Every case compares every output element; the full-size workloads also hold
+each (b, h_kv) unit to the rel-L2 bound on its own.  Outputs are pre-filled with
 NaN and the workspace with NaN bit patterns, so an element the kernels never
 write, or a partial read before it is written, fails.
 """
@@ -11,7 +11,7 @@ import pytest
 import oracle
 import workloads
 from golden_util import attn_case, expected, load
-from gpu_util import DevCase, assert_attn_close, to_f64
+from gpu_util import DevCase, assert_attn_close, assert_attn_units, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def _run_full(c, what=""):
     dc = DevCase(c)
     got = to_f64(dc.attn(), c.dtype)
     ref = oracle.block_attn(c)
-    return assert_attn_close(got, ref, c.dtype, what)
+    return assert_attn_units(got, ref, c.Hkv, c.dtype, what)
 
 
 def _case(seed, B, S, Hq, Hkv, D, lens, ps, dtype="bf16", **kw):
@@ -140,38 +140,27 @@ def test_gqa_equals_mha_with_repeated_kv():
     np.testing.assert_allclose(gq, mh, rtol=0, atol=1e-2)
 
 
-# ------------------------------------------------------------ full-size workloads, sampled rows
+# ------------------------------------------------------------ full-size workloads, whole tensor
 
-def _sample_rows(c, rng, n_random=192):
-    rows = set()
-    order = np.argsort(c.ctx_lens)
-    for b in (int(order[0]), int(order[-1])):          # shortest and longest sequence
-        for t in range(c.S):
-            for h in range(c.Hq):
-                if (t * c.Hq + h) % 7 == 0:
-                    rows.add((b, t, h))
-    for _ in range(n_random):
-        rows.add((int(rng.integers(c.B)), int(rng.integers(c.S)), int(rng.integers(c.Hq))))
-    return sorted(rows)
-
-
-def _sampled_parity(c, name):
+def _whole_parity(c, name):
+    """Every output element against the oracle (run on all host threads),
+    with the rel-L2 bound applied per (b, h_kv) unit as well."""
     dc = DevCase(c)
     out = to_f64(dc.attn(), "bf16")
-    assert np.isfinite(out).all(), name + ": unwritten outputs"
-    rows = _sample_rows(c, np.random.Generator(np.random.PCG64(c.seed + 100)))
-    ref = oracle.block_attn(c, rows=rows)
-    got = np.stack([out[b, t, h] for b, t, h in rows])
-    assert_attn_close(got, ref, "bf16", name + " sampled rows")
+    ref = oracle.block_attn(c)
+    assert_attn_units(out, ref, c.Hkv, "bf16", name)
 
 
+@pytest.mark.timeout(300)
 def test_config2_full_size():
-    _sampled_parity(workloads.config2(), "config2 B=8 L=4096")
+    _whole_parity(workloads.config2(), "config2 B=8 L=4096")
 
 
+@pytest.mark.timeout(600)
 def test_config3_full_size():
-    _sampled_parity(workloads.config3(), "config3 B=64 ragged 1K..16K")
+    _whole_parity(workloads.config3(), "config3 B=64 ragged 1K..16K")
 
 
+@pytest.mark.timeout(600)
 def test_config4_full_size():
-    _sampled_parity(workloads.config4(), "config4 B=4 L=65536")
+    _whole_parity(workloads.config4(), "config4 B=4 L=65536")

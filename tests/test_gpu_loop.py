@@ -6,7 +6,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import DevCase, assert_attn_close, assert_commit_ok, dev_tensor, to_f64, torch_mod
+from gpu_util import (DevCase, assert_attn_close, assert_attn_units, assert_commit_ok, dev_tensor,
+                      to_f64, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -146,22 +147,21 @@ def test_reduced_denoise_loop():
         assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
 
 
-def test_full_size_denoise_loop_sampled():
+@pytest.mark.timeout(900)
+def test_full_size_denoise_loop():
     """config5 at full size: B=32, 6 layers, T=4, V=131072.  Unmask ids exact
-    every step, sampled attention rows per layer at the first and last step,
-    appended slots bit-exact."""
+    every step; every layer's attention at every step compared element by
+    element with the oracle, and per (b, h_kv) unit; appended slots
+    bit-exact."""
     lp = workloads.config5()
-    got = run_loop_gpu_sampled(lp)
+    got = run_loop_gpu_full(lp)
     assert got is None
 
 
-def run_loop_gpu_sampled(lp):
+def run_loop_gpu_full(lp):
     import two_tower_attention_amd as tt
     torch = torch_mod()
     B, S, T = lp.B, lp.S, lp.steps
-    rng = np.random.Generator(np.random.PCG64(55))
-    rows = sorted({(int(rng.integers(B)), int(rng.integers(S)), int(rng.integers(lp.Hq)))
-                   for _ in range(48)})
     devs = [DevCase(p) for p in lp.pools]
     mask_h = np.ones((B, S), np.uint8)
     mask = torch.ones((B, S), dtype=torch.uint8, device="cuda")
@@ -173,12 +173,10 @@ def run_loop_gpu_sampled(lp):
             kb = dev_tensor(lp.k_blk[s][i], "bf16")
             vb = dev_tensor(lp.v_blk[s][i], "bf16")
             out = to_f64(d.attn(q=q, k_blk=kb, v_blk=vb), "bf16")
-            assert np.isfinite(out).all()
-            if s in (0, T - 1):
-                ref = oracle.block_attn(lp.pools[i], rows=rows, q=lp.q[s][i],
-                                        k_blk=lp.k_blk[s][i], v_blk=lp.v_blk[s][i])
-                assert_attn_close(np.stack([out[b, t, h] for b, t, h in rows]), ref, "bf16",
-                                  "full loop step %d layer %d" % (s, i))
+            ref = oracle.block_attn(lp.pools[i], q=lp.q[s][i], k_blk=lp.k_blk[s][i],
+                                    v_blk=lp.v_blk[s][i])
+            assert_attn_units(out, ref, lp.pools[i].Hkv, "bf16",
+                              "full loop step %d layer %d" % (s, i))
         lg = dev_tensor(lp.logits[s], "f32")
         ids = torch.empty((B, S), dtype=torch.int32, device="cuda")
         com = torch.empty((B, S), dtype=torch.uint8, device="cuda")
