@@ -18,6 +18,13 @@ streams from HBM.
 The dominant kernel (block attention) is timed again on its own with HIP
 events (rotating over the 24 (step, layer) inputs) for the roofline entry;
 the CPU oracle is timed on a bounded sample for the cpu_baseline entry.
+
+The same line carries block attention alone at the other measured shapes
+(configs 2-4: B=8 x 4K, a ragged B=64 batch of 1K-16K contexts, B=4 x 64K),
+each with inputs rotated over more than 768 MB so that the Infinity Cache
+cannot serve them, against the HBM and MFMA peaks and a measured copy rate;
+and the oracle timed over whole configs 1-4 on all host threads (configs 1
+and 2 also on one).  `--config N` runs config N's attention alone.
 """
 import argparse
 import hashlib
@@ -34,7 +41,21 @@ if ROOT not in sys.path:
 METRIC = ("block-attn HBM GB/s & TFLOP/s (fraction of peak); denoise-steps/sec, 1 GPU")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_split_config5_counters.md")
+# bytes the rotating input sets of a config total at least: three times the
+# 256 MB Infinity Cache, so every launch streams its inputs from HBM
+ROT_BYTES = 768 * 10 ** 6
+ATTN_WORKLOADS = {
+    2: "block attention, B=8, S=16, H_q=32, H_kv=2, D=128, L=4096 each, 256-token bf16 pages",
+    3: ("block attention, ragged decode batch: B=64, S=16, H_q=32, H_kv=2, D=128, L uniform over "
+        "multiples of 16 in [1024, 16384], 256-token bf16 pages"),
+    4: "block attention, long context: B=4, S=16, H_q=32, H_kv=2, D=128, L=65536 each, 256-token bf16 pages",
+    5: ("block attention of one denoise-loop layer: B=32, S=16, H_q=32, H_kv=2, D=128, L uniform over "
+        "multiples of 16 in [2048, 8192], 256-token bf16 pages"),
+}
+
+
+def counters_file(cfg):
+    return os.path.join(ROOT, "profiles", "attn_split_config%d_counters.md" % cfg)
 
 
 def log(msg):
@@ -49,13 +70,15 @@ def attn_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic(bytes_alg):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTERS_FILE):
+def read_traffic(cfg):
+    """HBM bytes per launch of a config's attention from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
+    path = counters_file(cfg)
+    if not os.path.exists(path):
         return None
     rec = None
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if line.startswith("COUNTERS_JSON "):
                 rec = json.loads(line[len("COUNTERS_JSON "):])
@@ -90,7 +113,7 @@ def _read_counters(path, counter):
     return per
 
 
-def summarize_pmc(fetch_csv, write_csv, out_md, command=""):
+def summarize_pmc(fetch_csv, write_csv, out_md, command="", cfg=5):
     fetch = _read_counters(fetch_csv, "FETCH_SIZE")
     write = _read_counters(write_csv, "WRITE_SIZE")
     # the calibration copy is the largest copy dispatch
@@ -98,9 +121,10 @@ def summarize_pmc(fetch_csv, write_csv, out_md, command=""):
     kib = CALIB_BYTES / 1024.0
     sf, sw = kib / cf, kib / cw
     rec = {"source_hash": attn_source_hash(), "fetch_scale": sf, "write_scale": sw}
-    lines = ["# Attention HBM traffic counters (config-5 layer launch)", "",
+    lines = ["# Attention HBM traffic counters (config %d)" % cfg, "",
+             "Workload: %s." % ATTN_WORKLOADS[cfg], "",
              "Counters from two `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per",
-             "dispatch) over `python3 bench.py --only-attn`, scaled by the same counter on a plain",
+             "dispatch) over `python3 bench.py --config %d --only-attn`, scaled by the same counter on a plain" % cfg,
              "256 MiB device copy (fetch scale %.4f, write scale %.4f)." % (sf, sw), "",
              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) |",
              "|---|---|---|---|---|"]
@@ -201,9 +225,142 @@ def lmhead_bench(np, torch, tt, workloads, dev, B=32, S=16, H=4096, V=131072, it
             "weights": "synthetic: hidden ~ N(0,1), head ~ N(0, 9/H), so logits ~ N(0, 3^2)"}
 
 
+def attn_bytes_flops(np, c):
+    """Algorithmic bytes (context K/V once, Q and O, the block's K/V) and
+    flops (Q.K^T and P.V over context plus block keys) of one launch."""
+    lens = c.ctx_lens.astype(np.int64)
+    kv = int(lens.sum()) * c.Hkv * c.D * 2 * 2
+    qo = 2 * c.B * c.S * c.Hq * c.D * 2
+    blk = 2 * c.B * c.S * c.Hkv * c.D * 2
+    flops = 4 * c.D * c.S * c.Hq * int((lens + c.S).sum())
+    return kv + qo + blk, flops
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, iters=10):
+    """Device-to-device copy of 1 GiB (read + write counted): the streaming
+    rate a plain copy kernel reaches on this GPU."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / iters
+    del src, dst
+    return {"GB/s": 2.0 * nbytes / t / 1e9, "bytes_per_copy": 2 * nbytes,
+            "kernel": "torch device-to-device copy_ of 1 GiB fp32 (read + write bytes)"}
+
+
+def attn_config_bench(np, torch, tt, workloads, dev, cfg, copy_gbs, iters=48, graph=True):
+    """One config's block attention timed alone: inputs rotated over enough
+    device copies that they total more than ROT_BYTES, HIP events on the
+    launch stream around `iters` launches (eager, then replayed from a HIP
+    graph)."""
+    c = {2: workloads.config2, 3: workloads.config3, 4: workloads.config4}[cfg]()
+    nbytes, flops = attn_bytes_flops(np, c)
+    copies = ROT_BYTES // nbytes + 1
+    iters = -(-max(iters, copies) // copies) * copies
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = [bf(c.q), bf(c.k_blk), bf(c.v_blk), bf(c.k_pages), bf(c.v_pages),
+            torch.from_numpy(c.page_table).to(dev), torch.from_numpy(c.ctx_lens).to(dev)]
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    desc = tt.make_desc(c.B, c.S, c.Hq, c.Hkv, c.D, c.page_size, c.page_table.shape[1],
+                        c.k_pages.shape[0], int(c.ctx_lens.max()))
+    out = torch.empty((c.B, c.S, c.Hq, c.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(tt.tt_block_attn_workspace_bytes(desc), 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def loop():
+        for it in range(iters):
+            tt.tt_block_attn(desc, *sets[it % copies], out, ws)
+
+    loop()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    loop()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_eager = e0.elapsed_time(e1) / 1e3 / iters
+    t = t_eager
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(stream)
+        with torch.cuda.stream(s_cap):
+            with torch.cuda.graph(g, stream=s_cap):
+                loop()
+        stream.wait_stream(s_cap)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / iters
+        del g
+    gbs, tfs = nbytes / t / 1e9, flops / t / 1e12
+    lens = c.ctx_lens.astype(np.int64)
+    res = {"workload": ATTN_WORKLOADS[cfg], "us_per_launch": t * 1e6,
+           "us_per_launch_eager": t_eager * 1e6, "launches_timed": iters,
+           "alg_bytes_per_launch": nbytes, "alg_flops_per_launch": flops,
+           "GB/s": gbs, "TFLOP/s": tfs, "frac_hbm": gbs / HBM_PEAK_GBS,
+           "frac_mfma": tfs / MFMA_BF16_PEAK_TFLOPS,
+           "frac_copy": gbs / copy_gbs if copy_gbs else None,
+           "mean_ctx_len": float(lens.mean()), "seed": c.seed,
+           "rotation": {"sets": copies, "bytes": copies * nbytes},
+           "traffic": read_traffic(cfg), "timing": "graph replay" if graph else "eager"}
+    log("config %d attention: %.1f us/launch (eager %.1f), %.0f GB/s (%.2f of HBM, %.2f of copy), "
+        "%.0f TFLOP/s; %d rotating sets" % (cfg, t * 1e6, t_eager * 1e6, gbs, gbs / HBM_PEAK_GBS,
+                                             res["frac_copy"] or 0.0, tfs, copies))
+    del sets, base, out, ws
+    return res
+
+
+def oracle_timings(np, workloads, configs=(1, 2, 3, 4), single=(1, 2)):
+    """The fp64 CPU oracle's block attention over whole configs (every query
+    row), on all OpenMP threads and, for the small configs, on one."""
+    import oracle
+    makers = {1: lambda: workloads.config1()[0], 2: workloads.config2, 3: workloads.config3,
+              4: workloads.config4}
+    nthr = oracle.num_threads()
+    res = {"threads": nthr, "kind": "oracle",
+           "what": "oracle.block_attn over every query row of the config (fp64 C, OpenMP)"}
+
+    def one(c, threads):
+        with oracle.threads(threads):
+            t0 = time.perf_counter()
+            oracle.block_attn(c)
+            dt = time.perf_counter() - t0
+        rows = c.B * c.S * c.Hq
+        return {"s": dt, "threads": threads, "rows": rows, "rows_per_s": rows / dt}
+
+    for k in configs:
+        c = makers[k]()
+        res["config%d" % k] = one(c, nthr)
+        if k in single:
+            res["config%d_1thread" % k] = one(c, 1)
+        log("oracle config %d: %.2f s on %d threads%s" % (
+            k, res["config%d" % k]["s"], nthr,
+            (", %.2f s on 1" % res["config%d_1thread" % k]["s"]) if k in single else ""))
+        del c
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--config", type=int, default=5, choices=(2, 3, 4, 5),
+                    help="5: the denoise loop (headline line, with configs 2-4 as attention "
+                         "entries); 2, 3, 4: that config's block attention alone")
     ap.add_argument("--steps", type=int, default=20, help="timed blocks (4 denoise steps each)")
     # the matrix cores' clock ramps up over the first tens of milliseconds of
     # sustained load; 20 untimed blocks (about 36 ms) reach the steady state
@@ -225,9 +382,11 @@ def main():
                     help="turn a rocprofv3 --stats kernel_stats.csv into a summary")
     ap.add_argument("--profile-command", default="",
                     help="command line recorded in a --summarize-* summary")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the config 2-4 attention entries and the oracle timings")
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(*args.summarize_pmc, command=args.profile_command)
+        summarize_pmc(*args.summarize_pmc, command=args.profile_command, cfg=args.config)
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats, command=args.profile_command)
@@ -256,6 +415,9 @@ def main():
 
     if args.only_lmhead:
         print(json.dumps({"lmhead_unmask": lmhead_bench(np, torch, tt, workloads, dev)}), flush=True)
+        return
+    if args.config != 5:
+        config_main(args, np, torch, tt, workloads, dev)
         return
 
     t_gen = time.perf_counter()
@@ -344,6 +506,9 @@ def main():
     # the eagerly launched figure is reported beside it.
     stream = torch.cuda.current_stream()
     ctx.copy_(ctx0)
+    copy_bw = None if args.only_attn else copy_bandwidth(torch, dev)
+    if copy_bw:
+        log("copy bandwidth: %.0f GB/s" % copy_bw["GB/s"])
     for it in range(6):
         attn(it % T, it % NL)
     torch.cuda.synchronize()
@@ -531,8 +696,20 @@ def main():
                              c_attn + c_un))}
         log("cpu oracle: %.2f s per denoise step (extrapolated from %.1f s)" % (step_s, c_attn + c_un))
 
+    # ---- configs 2-4: block attention alone at the other measured shapes,
+    # and the oracle over whole configs
+    configs = None
+    oracle_t = None
+    if extras and not args.no_configs:
+        configs = {}
+        for k in (2, 3, 4):
+            configs["config%d" % k] = attn_config_bench(np, torch, tt, workloads, dev, k,
+                                                        copy_bw["GB/s"], graph=not args.no_graph)
+        if not args.no_cpu_baseline:
+            oracle_t = oracle_timings(np, workloads)
+
     steps_per_s = T / block_s
-    traffic = read_traffic(attn_bytes)
+    traffic = read_traffic(5)
     res = {
         "metric": METRIC,
         "value": steps_per_s,
@@ -541,6 +718,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": block_s * 1e3,
+        "blocks_timed": args.steps,
+        "ms_per_denoise_step": block_s / T * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -554,6 +733,7 @@ def main():
                    "parallelism": "none (1 GPU)", "seed": lp.seed},
         "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": attn_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac_copy": attn_gbs / copy_bw["GB/s"] if copy_bw else None,
                      "kernel": "tt_block_attn (split + combine launches)",
                      "us_per_launch": attn_s * 1e6, "us_per_launch_eager": attn_eager_s * 1e6,
                      "alg_bytes_per_launch": attn_bytes,
@@ -564,6 +744,55 @@ def main():
         "chunk_attn": chunk,
         "block_sizes": block_sizes,
         "lmhead_unmask": lm,
+        "copy_bandwidth": copy_bw,
+        "attn_configs": configs,
+        "oracle_timings": oracle_t,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def config_main(args, np, torch, tt, workloads, dev):
+    """--config 2, 3 or 4: that config's block attention alone, one JSON line
+    (value = algorithmic GB/s).  With --only-attn (counter runs): the
+    launches eagerly, then one 256 MiB calibration copy."""
+    if args.only_attn:
+        attn_config_bench(np, torch, tt, workloads, dev, args.config, None, graph=False)
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        return
+    copy_bw = copy_bandwidth(torch, dev)
+    log("copy bandwidth: %.0f GB/s" % copy_bw["GB/s"])
+    r = attn_config_bench(np, torch, tt, workloads, dev, args.config, copy_bw["GB/s"],
+                          graph=not args.no_graph)
+    cpu = None
+    if not args.no_cpu_baseline:
+        ot = oracle_timings(np, workloads, configs=(args.config,),
+                            single=(args.config,) if args.config == 2 else ())
+        o = ot["config%d" % args.config]
+        cpu = {"value": r["alg_bytes_per_launch"] / o["s"] / 1e9, "unit": "GB/s",
+               "cores": o["threads"], "kind": "oracle",
+               "sample": "the whole config (%d query rows) through oracle.block_attn in %.2f s, "
+                         "scaled to the same algorithmic bytes" % (o["rows"], o["s"]),
+               "timings": ot}
+    res = {
+        "metric": "block-attn HBM GB/s (fraction of peak), config %d, 1 GPU" % args.config,
+        "value": r["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": r["launches_timed"],
+        "warmup": r["launches_timed"], "ms_per_step": r["us_per_launch"] / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": r["workload"], "mean_ctx_len": r["mean_ctx_len"], "seed": r["seed"],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": r["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": r["frac_hbm"], "traffic": r["traffic"], "frac_copy": r["frac_copy"],
+                     "kernel": "tt_block_attn (split + combine launches)",
+                     "us_per_launch": r["us_per_launch"], "alg_bytes_per_launch": r["alg_bytes_per_launch"],
+                     "tflops": r["TFLOP/s"], "mfma_frac": r["frac_mfma"]},
+        "cpu_baseline": cpu,
+        "attn": r,
+        "copy_bandwidth": copy_bw,
     }
     print(json.dumps(res), flush=True)
 

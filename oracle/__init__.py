@@ -73,6 +73,8 @@ def _load():
         lib.tto_unmask_f64.restype = I
         lib.tto_num_threads.argtypes = []
         lib.tto_num_threads.restype = I
+        lib.tto_set_num_threads.argtypes = [I]
+        lib.tto_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -98,6 +100,22 @@ class library:
 
 def num_threads() -> int:
     return int(_load().tto_num_threads())
+
+
+class threads:
+    """Context manager: run the oracle on n OpenMP threads inside the block."""
+
+    def __init__(self, n: int):
+        self.n = int(n)
+
+    def __enter__(self):
+        self._saved = num_threads()
+        _load().tto_set_num_threads(self.n)
+        return self
+
+    def __exit__(self, *exc):
+        _load().tto_set_num_threads(self._saved)
+        return False
 
 
 def _ptr(a: Optional[np.ndarray]):

@@ -376,3 +376,14 @@ int tto_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads later calls use (n >= 1), for timing the
+   oracle on one thread as well as on all of them. */
+void tto_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
