@@ -147,6 +147,108 @@ def summarize_pmc(fetch_csv, write_csv, out_md, command="", cfg=5):
     print("\n".join(lines))
 
 
+def _short_kernel(name):
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    cut = [i for i in (n.find("("), n.find("<")) if i > 0]
+    return (n[:min(cut)] if cut else n)[:60]
+
+
+def summarize_pmc_all(fetch_csv, write_csv, out_md, title, command=""):
+    """Every kernel's mean FETCH_SIZE / WRITE_SIZE per dispatch, scaled by
+    what the counters read for the run's 256 MiB calibration copy (its
+    largest copy dispatch)."""
+    import csv
+    data = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = _short_kernel(r["Kernel_Name"])
+                data.setdefault(k, {}).setdefault(counter, []).append(float(r["Counter_Value"]))
+    copies = [k for k in data if "copy" in k.lower() or "Copy" in k]
+    cf = max(max(data[k].get("FETCH_SIZE", [0])) for k in copies)
+    cw = max(max(data[k].get("WRITE_SIZE", [0])) for k in copies)
+    kib = CALIB_BYTES / 1024.0
+    sf, sw = kib / cf, kib / cw
+    lines = ["# %s" % title, "",
+             "Counters from two `rocprofv3 --pmc` passes (FETCH_SIZE, then WRITE_SIZE, KiB per",
+             "dispatch, mean over dispatches), scaled by the same counter on the run's plain",
+             "256 MiB device copy (fetch scale %.4f, write scale %.4f)." % (sf, sw), "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB (scaled) | HBM write MB (scaled) |",
+             "|---|---|---|---|---|---|"]
+    rows = []
+    for k, v in data.items():
+        f = v.get("FETCH_SIZE", [0.0])
+        w = v.get("WRITE_SIZE", [0.0])
+        fm, wm = sum(f) / len(f), sum(w) / len(w)
+        rows.append((fm * sf + wm * sw, k, len(f), fm, wm))
+    for _, k, n, fm, wm in sorted(rows, reverse=True)[:16]:
+        lines.append("| %s | %d | %.0f | %.0f | %.1f | %.1f |" % (
+            k, n, fm, wm, fm * sf * 1024 / 1e6, wm * sw * 1024 / 1e6))
+    if command:
+        lines += ["", "Commands (run from /tmp on the GPU host, REPO = the repository root):", "",
+                  "```", command, "```"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_sq(csv_a, csv_b, out_md, cfg, command=""):
+    """The attention split kernel's SQ counters (two passes of 8) and the
+    ratios that locate its bound: wait and issue stalls per wave cycle, MFMA
+    busy per SIMD cycle, LDS instructions per MFMA, bank conflicts."""
+    import csv
+    vals = {}
+    for path in (csv_a, csv_b):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if "attn_split_kernel" in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    m = {k: sum(v) / len(v) for k, v in vals.items()}
+    ndisp = len(vals.get("SQ_WAVES", []))
+    lines = ["# Attention split kernel: SQ counters (config %d)" % cfg, "",
+             "Workload: %s." % ATTN_WORKLOADS[cfg], "",
+             "Two `rocprofv3 --pmc` passes of 8 SQ counters each over `python3 bench.py --config %d "
+             "--only-attn` (%d dispatches of `attn_split_kernel`; mean per dispatch, totals over the "
+             "chip)." % (cfg, ndisp), "", "| counter | mean per dispatch |", "|---|---|"]
+    for k in sorted(m):
+        lines.append("| %s | %.4g |" % (k, m[k]))
+    g = lambda k: m.get(k, float("nan"))
+    lines += ["", "Derived (ratios of counters in the same unit):", "", "| quantity | value |", "|---|---|",
+              "| MFMA instructions per launch | %.3g M |" % (g("SQ_INSTS_MFMA") / 1e6),
+              "| LDS instructions per MFMA instruction (SQ_INSTS_LDS / SQ_INSTS_MFMA) | %.2f |"
+              % (g("SQ_INSTS_LDS") / g("SQ_INSTS_MFMA")),
+              "| VALU instructions per MFMA instruction (SQ_INSTS_VALU / SQ_INSTS_MFMA) | %.2f |"
+              % (g("SQ_INSTS_VALU") / g("SQ_INSTS_MFMA")),
+              "| wave cycles waiting at s_waitcnt (SQ_WAIT_ANY / SQ_WAVE_CYCLES) | %.0f%% |"
+              % (100 * g("SQ_WAIT_ANY") / g("SQ_WAVE_CYCLES")),
+              "| wave cycles not issuing (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) | %.0f%% |"
+              % (100 * g("SQ_WAIT_INST_ANY") / g("SQ_WAVE_CYCLES")),
+              "| wave cycles waiting to issue an LDS instruction (SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES) | %.1f%% |"
+              % (100 * g("SQ_WAIT_INST_LDS") / g("SQ_WAVE_CYCLES")),
+              "| LDS bank conflict cycles per LDS-active cycle (SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS) | %.1f%% |"
+              % (100 * g("SQ_LDS_BANK_CONFLICT") / g("SQ_ACTIVE_INST_LDS")),
+              "| MFMA busy per SIMD cycle (SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES)) | %.0f%% |"
+              % (100 * g("SQ_VALU_MFMA_BUSY_CYCLES") / (4 * g("SQ_BUSY_CU_CYCLES")))]
+    if command:
+        lines += ["", "Commands (run from /tmp on the GPU host, REPO = the repository root):", "",
+                  "```", command, "```"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def calibration_copy(torch, dev):
+    """A plain 256 MiB device copy: the reference dispatch for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a run."""
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def summarize_stats(stats_csv, out_md, command=""):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
@@ -378,6 +480,10 @@ def main():
                          "section's JSON)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files into a summary")
+    ap.add_argument("--summarize-pmc-all", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "TITLE"),
+                    help="every kernel's FETCH_SIZE / WRITE_SIZE from two counter runs")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("CSV_A", "CSV_B", "OUT_MD"),
+                    help="the attention split kernel's SQ counters from two counter runs")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a summary")
     ap.add_argument("--profile-command", default="",
@@ -387,6 +493,12 @@ def main():
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, command=args.profile_command, cfg=args.config)
+        return
+    if args.summarize_pmc_all:
+        summarize_pmc_all(*args.summarize_pmc_all, command=args.profile_command)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq, cfg=args.config, command=args.profile_command)
         return
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats, command=args.profile_command)
@@ -415,6 +527,7 @@ def main():
 
     if args.only_lmhead:
         print(json.dumps({"lmhead_unmask": lmhead_bench(np, torch, tt, workloads, dev)}), flush=True)
+        calibration_copy(torch, dev)
         return
     if args.config != 5:
         config_main(args, np, torch, tt, workloads, dev)
@@ -506,7 +619,7 @@ def main():
     # the eagerly launched figure is reported beside it.
     stream = torch.cuda.current_stream()
     ctx.copy_(ctx0)
-    copy_bw = None if args.only_attn else copy_bandwidth(torch, dev)
+    copy_bw = None if (args.only_attn or args.core) else copy_bandwidth(torch, dev)
     if copy_bw:
         log("copy bandwidth: %.0f GB/s" % copy_bw["GB/s"])
     for it in range(6):
@@ -650,12 +763,7 @@ def main():
             "(mean %.2f per sequence)" % (th_s * 1e6, th_gbs, sampler_steps, steps_per_seq.mean()))
     lm = lmhead_bench(np, torch, tt, workloads, dev) if extras else None
     if args.only_attn:
-        # calibration for FETCH_SIZE / WRITE_SIZE: a plain device copy of 256 MiB
-        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copy(torch, dev)   # for scaling FETCH_SIZE / WRITE_SIZE
         log("attention algorithmic bytes per launch: %d" % attn_bytes)
         return
 
@@ -749,6 +857,8 @@ def main():
         "oracle_timings": oracle_t,
     }
     print(json.dumps(res), flush=True)
+    if args.core:
+        calibration_copy(torch, dev)   # for scaling FETCH_SIZE / WRITE_SIZE
 
 
 def config_main(args, np, torch, tt, workloads, dev):
@@ -757,11 +867,7 @@ def config_main(args, np, torch, tt, workloads, dev):
     launches eagerly, then one 256 MiB calibration copy."""
     if args.only_attn:
         attn_config_bench(np, torch, tt, workloads, dev, args.config, None, graph=False)
-        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copy(torch, dev)
         return
     copy_bw = copy_bandwidth(torch, dev)
     log("copy bandwidth: %.0f GB/s" % copy_bw["GB/s"])
