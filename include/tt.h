@@ -31,6 +31,19 @@
  *     enqueue only kernel launches, so they can be captured in a HIP graph
  *     and replayed; the first call on each device also sets a kernel
  *     attribute, so make one call before capturing.
+ *
+ * Choices of this ABI that callers must honour (the pages fix none of them):
+ *   - Cached VALUES are feature-major inside a page, v_pages [P, H_kv, D,
+ *     page_size], while cached keys are token-major, k_pages [P, H_kv,
+ *     page_size, D].  A writer of the value pool other than tt_kv_append
+ *     must use this layout: it gives P.V its matrix-core operands as
+ *     contiguous 16-byte runs.
+ *   - page_size is a power of two (16..4096), not any multiple of 16, so
+ *     that token -> (page, offset) is a shift and a mask on the device.
+ *   - The workspace-size queries return a tt_status and report the size
+ *     through an out-parameter, so that a bad shape is an error, not 0.
+ *   - tt_attn_desc carries num_pages, the pool size, so that page ids can be
+ *     bounds-clamped on the device.
  */
 #ifndef TT_H
 #define TT_H
