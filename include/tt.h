@@ -24,8 +24,9 @@
  *     the device so that bad values never fault; results are then
  *     unspecified.  tt_kv_append skips a sequence whose target slots are not
  *     all backed by valid pages.
- *   - Calls are stateless apart from a per-thread error string; concurrent
- *     calls on different streams must not share a workspace.
+ *   - Calls are stateless apart from a per-thread error string (and the
+ *     static array of tt_unmask_noalloc); concurrent calls on different
+ *     streams must not share a workspace.
  *   - Results are bitwise reproducible for the same inputs and shapes (fixed
  *     reduction orders, no atomics on data).  The calls allocate nothing and
  *     enqueue only kernel launches, so they can be captured in a HIP graph
@@ -214,6 +215,26 @@ int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit,
               int32_t remaining_steps, int32_t batch, int32_t block, int32_t vocab,
               int32_t *ids_out, uint8_t *commit_out, float *conf_out, uint32_t flags,
               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tt_unmask for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument.  Arguments, results and errors as tt_unmask.  The row partials
+ * live in a static device array of TT_UNMASK_NOALLOC_MAX_BYTES (1 MiB) that
+ * every device the library runs on holds until the process ends.  Every
+ * shape tt_unmask accepts fits (its tt_unmask_workspace_bytes is at most
+ * 16 x max(batch * block, 1023) bytes); a larger need would fail with
+ * TT_ERR_WORKSPACE before any device work.  The array needs no
+ * initial contents, but every call on a device shares it: calls that may
+ * overlap on one device (unordered streams) race; calls ordered on one
+ * stream do not.  The first call on each device looks up the array's
+ * address; make one call there before capturing a graph.
+ */
+#define TT_UNMASK_NOALLOC_MAX_BYTES (1u << 20)
+int tt_unmask_noalloc(const float *logits, uint8_t *mask, const int32_t *k_commit,
+                      int32_t remaining_steps, int32_t batch, int32_t block, int32_t vocab,
+                      int32_t *ids_out, uint8_t *commit_out, float *conf_out, uint32_t flags,
+                      void *stream);
 
 /*
  * Threshold form of the commit rule, the one the pages' sampler uses

@@ -175,6 +175,35 @@ def test_unmask_nulls(lib):
     assert st == -1
 
 
+@pytest.mark.parametrize("name,kw,code", UNMASK_BAD, ids=[u[0] for u in UNMASK_BAD])
+def test_unmask_noalloc_validation(lib, name, kw, code):
+    """The no-workspace variant checks its arguments as tt_unmask does."""
+    a = dict(B=2, S=16, V=1024, rem=1, k=FAKE, flags=0)
+    a.update(kw)
+    st = lib.tt_unmask_noalloc(FAKE, FAKE, a["k"], a["rem"], a["B"], a["S"], a["V"], FAKE, FAKE,
+                               None, a["flags"], None)
+    assert st == code
+    assert lib.tt_unmask_noalloc(None, FAKE, FAKE, 1, 2, 16, 1024, FAKE, FAKE, None, 0, None) == -1
+    assert lib.tt_unmask_noalloc(FAKE, FAKE, FAKE, 1, 0, 16, 1024, FAKE, FAKE, None, 0, None) == 0
+
+
+def test_unmask_noalloc_static_scratch_holds_every_shape(lib):
+    """The static array (1 MiB) holds the row partials of every shape the
+    unmask accepts: the planner's need peaks at 16 B x max(B*S, 1023)."""
+    limit = 1 << 20
+    worst = 0
+    for rows in list(range(1, 1100)) + [4095, 4096, 20000, 65535]:
+        for S in (1, 16, 64):
+            if rows % S:
+                continue
+            for V in (1, 7, 1024, 131072, 2 ** 31 - 1):
+                n = ctypes.c_size_t(0)
+                assert lib.tt_unmask_workspace_bytes(rows // S, S, V, ctypes.byref(n)) == 0
+                worst = max(worst, n.value)
+                assert n.value <= 16 * max(rows, 1023) <= limit, (rows, S, V, n.value)
+    assert worst == 16 * 65535
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(tt.LibraryMissing):
         tt.load_library(str(tmp_path / "nope.so"))

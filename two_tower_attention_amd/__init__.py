@@ -24,7 +24,7 @@ TT_F32 = 1
 TT_UNMASK_UPDATE_MASK = 1
 
 EXPORTS = ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_chunk_attn", "tt_kv_append",
-           "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold",
+           "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_noalloc", "tt_unmask_threshold",
            "tt_lmhead_unmask_workspace_bytes", "tt_lmhead_unmask", "tt_lmhead_unmask_threshold",
            "tt_status_str",
            "tt_last_error", "tt_abi_version")
@@ -69,6 +69,7 @@ def load_library(path: Optional[str] = None):
     lib.tt_kv_append.argtypes = [DP, P, P, P, P, P, P, P]
     lib.tt_unmask_workspace_bytes.argtypes = [I32, I32, I32, ctypes.POINTER(SZ)]
     lib.tt_unmask.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, ctypes.c_uint32, P, SZ, P]
+    lib.tt_unmask_noalloc.argtypes = [P, P, P, I32, I32, I32, I32, P, P, P, ctypes.c_uint32, P]
     lib.tt_unmask_threshold.argtypes = [P, P, ctypes.c_float, I32, I32, I32, P, P, P, P,
                                         ctypes.c_uint32, P, SZ, P]
     lib.tt_lmhead_unmask_workspace_bytes.argtypes = [I32, I32, I32, I32, ctypes.POINTER(SZ)]
@@ -82,7 +83,7 @@ def load_library(path: Optional[str] = None):
     lib.tt_last_error.restype = ctypes.c_char_p
     lib.tt_abi_version.argtypes = []
     for name in ("tt_block_attn_workspace_bytes", "tt_block_attn", "tt_kv_append",
-                 "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_threshold",
+                 "tt_unmask_workspace_bytes", "tt_unmask", "tt_unmask_noalloc", "tt_unmask_threshold",
                  "tt_lmhead_unmask_workspace_bytes", "tt_lmhead_unmask",
                  "tt_lmhead_unmask_threshold", "tt_abi_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -219,6 +220,22 @@ def tt_unmask(logits, mask, k_commit, remaining_steps: int, ids_out, commit_out,
         _ptr(commit_out, "commit_out", torch.uint8, B * S),
         _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True), int(flags),
         _ptr(workspace, "workspace", allow_none=True), nbytes, _stream(stream)))
+
+
+def tt_unmask_noalloc(logits, mask, k_commit, remaining_steps: int, ids_out, commit_out,
+                      conf_out=None, flags: int = 0, stream=None) -> None:
+    """tt_unmask with its row partials in the library's static device array
+    (no workspace; see include/tt.h)."""
+    torch = _torch()
+    B, S = mask.shape
+    V = logits.shape[-1]
+    _check(load_library().tt_unmask_noalloc(
+        _ptr(logits, "logits", torch.float32, B * S * V), _ptr(mask, "mask", torch.uint8, B * S),
+        _ptr(k_commit, "k_commit", torch.int32, B, allow_none=True), int(remaining_steps),
+        B, S, V, _ptr(ids_out, "ids_out", torch.int32, B * S),
+        _ptr(commit_out, "commit_out", torch.uint8, B * S),
+        _ptr(conf_out, "conf_out", torch.float32, B * S, allow_none=True), int(flags),
+        _stream(stream)))
 
 
 def tt_unmask_threshold(logits, mask, gamma: float, ids_out, commit_out, conf_out=None,

@@ -222,21 +222,39 @@ int tt_unmask_workspace_bytes(int32_t B, int32_t S, int32_t V, size_t *bytes) {
   return ok();
 }
 
-int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit, int32_t remaining_steps,
-              int32_t B, int32_t S, int32_t V, int32_t *ids_out, uint8_t *commit_out,
-              float *conf_out, uint32_t flags, void *workspace, size_t workspace_bytes,
-              void *stream) {
+// Checks of tt_unmask's arguments other than the workspace; *done is set
+// when the call has nothing to do (B = 0).
+static int check_unmask_args(const float *logits, uint8_t *mask, const int32_t *k_commit,
+                             int32_t remaining_steps, int32_t B, int32_t S, int32_t V,
+                             int32_t *ids_out, uint8_t *commit_out, float *conf_out,
+                             uint32_t flags, bool *done) {
+  *done = false;
   int st = check_unmask_shape(B, S, V);
   if (st) return st;
   if (flags & ~TT_UNMASK_UPDATE_MASK) return fail(TT_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   if (!k_commit && remaining_steps < 1)
     return fail(TT_ERR_SHAPE, "remaining_steps %d < 1 with k_commit NULL", remaining_steps);
-  if (B == 0) return ok();
+  if (B == 0) {
+    *done = true;
+    return TT_OK;
+  }
   if (!logits || !mask || !ids_out || !commit_out)
     return fail(TT_ERR_NULL, "logits, mask, ids_out and commit_out are required");
   if (!aligned(logits, 4) || !aligned(ids_out, 4) || (k_commit && !aligned(k_commit, 4)) ||
       (conf_out && !aligned(conf_out, 4)))
     return fail(TT_ERR_UNSUPPORTED, "logits, ids_out, k_commit, conf_out must be 4-byte aligned");
+  return TT_OK;
+}
+
+int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit, int32_t remaining_steps,
+              int32_t B, int32_t S, int32_t V, int32_t *ids_out, uint8_t *commit_out,
+              float *conf_out, uint32_t flags, void *workspace, size_t workspace_bytes,
+              void *stream) {
+  bool done = false;
+  const int st = check_unmask_args(logits, mask, k_commit, remaining_steps, B, S, V, ids_out,
+                                   commit_out, conf_out, flags, &done);
+  if (st) return st;
+  if (done) return ok();
   const tt::UnmaskPlan plan = tt::plan_unmask(B, S, V);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(TT_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
@@ -246,6 +264,34 @@ int tt_unmask(const float *logits, uint8_t *mask, const int32_t *k_commit, int32
   const hipError_t e = tt::launch_unmask(plan, logits, mask, k_commit, remaining_steps, ids_out,
                                          commit_out, conf_out, flags, workspace,
                                          (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+static_assert(TT_UNMASK_NOALLOC_MAX_BYTES == tt::kUnmaskStaticBytes,
+              "the header states the static scratch size");
+
+int tt_unmask_noalloc(const float *logits, uint8_t *mask, const int32_t *k_commit,
+                      int32_t remaining_steps, int32_t B, int32_t S, int32_t V, int32_t *ids_out,
+                      uint8_t *commit_out, float *conf_out, uint32_t flags, void *stream) {
+  bool done = false;
+  const int st = check_unmask_args(logits, mask, k_commit, remaining_steps, B, S, V, ids_out,
+                                   commit_out, conf_out, flags, &done);
+  if (st) return st;
+  if (done) return ok();
+  const tt::UnmaskPlan plan = tt::plan_unmask(B, S, V);
+  if (plan.ws_bytes > tt::kUnmaskStaticBytes)
+    return fail(TT_ERR_WORKSPACE,
+                "tt_unmask_noalloc: batch %d x block %d x vocab %d needs %zu bytes of row partials, "
+                "its static scratch holds %zu; use tt_unmask with a workspace",
+                B, S, V, plan.ws_bytes, tt::kUnmaskStaticBytes);
+  if (device_cus(nullptr) <= 0) return fail(TT_ERR_NO_DEVICE, "no HIP device");
+  void *scratch = nullptr;
+  hipError_t e = tt::unmask_static_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(TT_ERR_LAUNCH, "address of the static scratch: %s", hipGetErrorString(e));
+  e = tt::launch_unmask(plan, logits, mask, k_commit, remaining_steps, ids_out, commit_out,
+                        conf_out, flags, scratch, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TT_ERR_LAUNCH, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -86,6 +86,14 @@ struct UnmaskPlan {
 
 UnmaskPlan plan_unmask(int B, int S, int V);
 
+// Size of the static row-partials array of tt_unmask_noalloc, and the
+// current device's address of it (looked up on the first call on each
+// device).  plan_unmask splits a row into ceil(512 / rows) chunks at most, so
+// rows * chunks < max(rows, 1024) <= 65535 partials of 16 bytes: 1 MiB holds
+// every shape the unmask accepts.
+constexpr size_t kUnmaskStaticBytes = size_t(1) << 20;
+hipError_t unmask_static_scratch(void **ptr);
+
 hipError_t launch_unmask(const UnmaskPlan &p, const float *logits, uint8_t *mask,
                          const int32_t *k_commit, int remaining_steps, int32_t *ids,
                          uint8_t *commit, float *conf, uint32_t flags, void *workspace,

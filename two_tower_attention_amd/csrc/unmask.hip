@@ -14,6 +14,8 @@
 // asc) and commits those ranked below k.
 #include <limits.h>
 
+#include <mutex>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -326,6 +328,36 @@ hipError_t launch_unmask_threshold(const UnmaskPlan &p, const float *logits, uin
   if (e != hipSuccess) return e;
   return launch_unmask_threshold_commit(parts, p.chunks, p.B, p.S, mask, gamma, ids, commit, conf,
                                         nsteps, flags, stream);
+}
+
+// Row partials of tt_unmask_noalloc: a static device array instead of a
+// caller workspace, for callers that cannot allocate.  Each device holds its
+// own copy until the process ends; in host code `scratch` names a host-side
+// stand-in, so kernels get the device address that
+// hipGetSymbolAddress reports, looked up once per device.
+__device__ __align__(256) unsigned char scratch[kUnmaskStaticBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+hipError_t unmask_static_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace tt
