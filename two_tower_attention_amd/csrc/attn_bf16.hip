@@ -57,6 +57,7 @@ constexpr int kMinTiles = 8;     // smallest range worth a work-group
 #define TT_ATTN_UNITPAD 4
 #endif
 constexpr int kUnitPad = TT_ATTN_UNITPAD;
+constexpr float kLazy = 8.0f;    // rescale when max grows by > 2^kLazy
 
 template <int D>
 struct Geo {
@@ -572,47 +573,10 @@ __device__ __forceinline__ void mfma_pv(const Batch &x, int b, const PTile<D> &P
   }
 }
 
-// Probabilities of a tile's scores relative to the reference `mref` (log2
-// units): P = 2^(s*sl2 - mref), rounded to bf16 for P.V.  Returns this
-// lane's sum of the rounded probabilities (the weights P.V actually uses),
-// taken with bf16 dot products in four chains.
-template <int D>
-__device__ __forceinline__ float tile_probs(const Params &p, const f32x16 (&s)[2], float mref,
-                                            PTile<D> &P) {
-  const float nm = -mref;
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    f32x16 e;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][r], p.sl2, nm));
-    const f32x8 lo = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
-    const f32x8 hi = {e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]};
-    P.v[tb][0] = __builtin_convertvector(lo, bf16x8);
-    P.v[tb][1] = __builtin_convertvector(hi, bf16x8);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 x = P.v[tb][c];
-      a[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1), one, a[0], false);
-      a[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3), one, a[1], false);
-      a[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5), one, a[2], false);
-      a[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7), one, a[3], false);
-    }
-  }
-  return (a[0] + a[1]) + (a[2] + a[3]);
-}
-
-// Online softmax of a tile's scores (log2 domain), returning P in bf16.
-// The reference `mref` stays where it is as long as the row's mass relative
-// to it (running sum plus this tile's) lies within [2^-40, 2^40]: then
-// neither the probabilities nor the sums can overflow or lose range, and no
-// row maximum is needed.  Otherwise (the unit's scores sit far from the
-// reference, typically only on its first tiles) the reference moves to the
-// larger of the tile's max and the log of the mass so far, the accumulators
-// are rescaled, and the tile's probabilities are recomputed.  Keys at or past
-// klim (per lane: the lane's query row) are masked when `mask`
-// (wave-uniform) is set.
+// Online softmax of a tile's scores (log2 domain): rescales the accumulators
+// when the running max grows by more than 2^kLazy, returns P in bf16.
+// Keys at or past klim (per lane: the lane's query row) are masked when
+// `mask` (wave-uniform) is set.
 template <int D>
 __device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2], int klim, bool mask,
                                              Acc<D> &A, PTile<D> &P) {
@@ -626,28 +590,37 @@ __device__ __forceinline__ void softmax_tile(const Params &p, f32x16 (&s)[2], in
       for (int r = 0; r < 16; ++r)
         if (32 * tb + 16 * (r >> 3) + (r & 7) >= lim) s[tb][r] = -INFINITY;
   }
-  float t = tile_probs<D>(p, s, A.mref, P);
-  const float lrow = pair_sum(A.lsum + t);
-  const bool ok = lrow >= 0x1p-40f && lrow <= 0x1p40f;  // false for inf and NaN
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(!ok) != 0, 0)) {
-    float mx = -INFINITY;
+  float mx = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tb][r]);
-    const float mxs = pair_max(mx) * p.sl2;
-    const float l0 = pair_sum(A.lsum);
-    const float meff = l0 > 0.f ? A.mref + __builtin_amdgcn_logf(l0) : -INFINITY;
-    float mnew = fmaxf(meff, mxs);
-    if (mnew == -INFINITY) mnew = A.mref;  // nothing seen yet: every key so far masked
-    const float f = l0 > 0.f ? __builtin_amdgcn_exp2f(A.mref - mnew) : 1.f;
-    A.mref = mnew;
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tb][r]);
+  mx = pair_max(mx);
+  const float mxs = mx * p.sl2;
+  const bool need = mxs > A.mref + kLazy;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float f = need ? __builtin_amdgcn_exp2f(A.mref - mxs) : 1.f;
+    if (need) A.mref = mxs;
     A.lsum *= f;
 #pragma unroll
     for (int db = 0; db < Geo<D>::DB; ++db) A.o[db] *= f;
-    t = tile_probs<D>(p, s, A.mref, P);
   }
-  A.lsum += t;
+  const float nm = -A.mref;
+  float acc = 0.f;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    f32x16 e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tb][r], p.sl2, nm));
+      acc += e[r];
+    }
+    const f32x8 lo = {e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]};
+    const f32x8 hi = {e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]};
+    P.v[tb][0] = __builtin_convertvector(lo, bf16x8);
+    P.v[tb][1] = __builtin_convertvector(hi, bf16x8);
+  }
+  A.lsum += acc;
 }
 
 // Score phase of a tile.  Expects its batch 0 in buf[0] (issued, not
@@ -852,7 +825,7 @@ __device__ void run_unit(const Params &p, const Unit &u, int i0, int i1, bool co
   Acc<D> A;
 #pragma unroll
   for (int db = 0; db < G::DB; ++db) A.o[db] = f32x16{};
-  A.mref = 0.f;  // any finite start: the first tile moves it if needed
+  A.mref = -INFINITY;
   A.lsum = 0.f;
   PTile<D> P;
 
