@@ -48,7 +48,7 @@ constexpr int kQRows = 256;      // query rows per unit
 constexpr int kThreads = 64 * (kQRows / 32);  // one wave per 32 query rows
 constexpr int kStages = TT_ATTN_STAGES;  // LDS ring depth (tiles in flight + 1)
 constexpr int kPageCache = 1024; // page ids cached per sub-range
-constexpr int kMinTiles = 8;     // smallest range worth a work-group
+constexpr int kMinTiles = 4;     // smallest range worth a work-group
 // Each unit carries kUnitPad virtual tiles after its real ones: they stand
 // for the unit's fixed cost (Q load, page-id cache, pipeline fill, block
 // tile, epilogue) so that ranges which cut unit boundaries get fewer real
