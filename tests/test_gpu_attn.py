@@ -164,3 +164,17 @@ def test_config3_full_size():
 @pytest.mark.timeout(600)
 def test_config4_full_size():
     _whole_parity(workloads.config4(), "config4 B=4 L=65536")
+
+
+@pytest.mark.timeout(900)
+def test_ranges_spanning_several_page_cache_fills():
+    """With 16-token pages a work-group caches the page ids of at most 255
+    tiles at a time, so a longer range is processed in several sub-ranges,
+    each refilling the cache from a different page base (pages of at least
+    256 tokens would need over a million tiles per launch for that).  B=1
+    with 16 KV heads of 256K tokens gives 65,616 flat tiles, more than
+    255 per work-group at up to 256 work-groups: every range crosses a
+    sub-range boundary, mostly in the middle of a page-table row."""
+    c = _case(77, 1, 16, 16, 16, 64, [262144], 16)
+    _run_full(c, "256K tokens, 16-token pages")
+
