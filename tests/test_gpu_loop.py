@@ -37,6 +37,8 @@ def test_kv_append_bit_exact(dtype, ps, lens):
 
 @pytest.mark.parametrize("dtype,S,Hkv,D,lens", [
     ("bf16", 64, 3, 128, [0, 200, 300]),   # one head is 16 KiB: passes of 2 heads, then 1
+    ("bf16", 20, 2, 64, [0, 8, 13, 232]),  # runs of 8 tokens and a 4-token tail; one unaligned start
+    ("f32", 23, 2, 64, [4, 12, 6]),        # runs of 4 tokens and a 3-token tail
     ("f32", 64, 3, 128, [64, 5, 511]),     # one head is 32 KiB: one head per pass
     ("bf16", 1, 5, 64, [0, 255, 256]),     # a one-token block, all 5 heads in one pass
 ])
@@ -54,20 +56,22 @@ def test_kv_append_head_passes(dtype, S, Hkv, D, lens):
     assert np.array_equal(_bits(dc.v_pages, dtype).view(np.uint8), vp.view(np.uint8))
 
 
-def test_kv_append_unaligned_block():
-    """Block keys that start off a 16-byte boundary take the element-wise path."""
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_kv_append_unaligned_block(which):
+    """Block keys or values that start off a 16-byte boundary take the element-wise path."""
     import two_tower_attention_amd as tt
     torch = torch_mod()
     rng = np.random.Generator(np.random.PCG64(21))
     c = workloads.make_attn_case(rng, B=2, S=16, Hq=4, Hkv=2, D=64, ctx_lens=[7, 300],
                                  page_size=256, extra_tokens=16)
     dc = DevCase(c)
-    n = dc.k_blk.numel()
-    buf = torch.empty(n + 1, dtype=dc.k_blk.dtype, device=dc.k_blk.device)
-    k_off = buf[1:].view(dc.k_blk.shape)   # 2 bytes past a 16-byte boundary
-    k_off.copy_(dc.k_blk)
-    assert k_off.data_ptr() % 16 != 0
-    tt.tt_kv_append(dc.desc, k_off, dc.v_blk, dc.k_pages, dc.v_pages, dc.page_table, dc.ctx_lens)
+    src = dc.k_blk if which == "k" else dc.v_blk
+    buf = torch.empty(src.numel() + 1, dtype=src.dtype, device=src.device)
+    off = buf[1:].view(src.shape)   # 2 bytes past a 16-byte boundary
+    off.copy_(src)
+    assert off.data_ptr() % 16 != 0
+    k_arg, v_arg = (off, dc.v_blk) if which == "k" else (dc.k_blk, off)
+    tt.tt_kv_append(dc.desc, k_arg, v_arg, dc.k_pages, dc.v_pages, dc.page_table, dc.ctx_lens)
     kp, vp, nl = oracle.kv_append(c.k_pages, c.v_pages, c.page_table, c.ctx_lens, c.k_blk, c.v_blk)
     assert np.array_equal(dc.ctx_lens.cpu().numpy(), nl)
     assert np.array_equal(_bits(dc.k_pages, "bf16").view(np.uint8), kp.view(np.uint8))
