@@ -90,21 +90,40 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendParams p) {
       // keys: token rows, 16-byte chunks straight to their page rows; values:
       // the same rows into LDS
       const int chunks = row / VEC;
-      for (int e = threadIdx.x, i = 0; e < p.S * chunks; e += kThreads, ++i) {
+      auto load = [&](int e, uint4 &k, uint4 &v) {
+        const int t = e / chunks, c = e % chunks;
+        const size_t src = ((size_t)t * p.Hkv + h0) * p.D + VEC * c;
+        k = *(const uint4 *)(kb + src);
+        v = *(const uint4 *)(vb + src);
+      };
+      auto store = [&](int e, const uint4 &k, const uint4 &v) {
         const int t = e / chunks, c = e % chunks;
         const int hh = (VEC * c) / p.D, d = (VEC * c) % p.D;
-        uint4 k, v;
-        if (h0 == 0 && i < kPre) {
-          k = pk[i];
-          v = pvv[i];
-        } else {
-          const size_t src = ((size_t)t * p.Hkv + h0) * p.D + VEC * c;
-          k = *(const uint4 *)(kb + src);
-          v = *(const uint4 *)(vb + src);
-        }
         const int pos = L + t;
         *(uint4 *)(kp + ((page_of(pos) * p.Hkv + h0 + hh) * p.page_size + pos % p.page_size) * p.D + d) = k;
         *(uint4 *)(sv + t * row + VEC * c) = v;
+      };
+      // the first kPre chunks of a thread, unrolled so that the prefetched
+      // registers are indexed by constants (a variable index would place
+      // them in scratch memory)
+#pragma unroll
+      for (int i = 0; i < kPre; ++i) {
+        const int e = threadIdx.x + i * kThreads;
+        if (e < p.S * chunks) {
+          uint4 k, v;
+          if (h0 == 0) {
+            k = pk[i];
+            v = pvv[i];
+          } else {
+            load(e, k, v);
+          }
+          store(e, k, v);
+        }
+      }
+      for (int e = threadIdx.x + kPre * kThreads; e < p.S * chunks; e += kThreads) {
+        uint4 k, v;
+        load(e, k, v);
+        store(e, k, v);
       }
     } else {
       for (int e = threadIdx.x; e < p.S * row; e += kThreads) {
