@@ -11,8 +11,9 @@
 // to 256 rows).  A unit's keys are cut into 64-token *tiles*: ceil(L_b/64)
 // context tiles, one tile holding the S block tokens, then kUnitPad virtual
 // tiles that only stand for the unit's fixed cost.  All tiles of all units
-// form one flat list; work-group w of G takes the contiguous range
-// [w*R, (w+1)*R), R = ceil(total/G).  Units wholly inside a range are
+// form one flat list; range w of G is [w*R, (w+1)*R), R = ceil(total/G),
+// and the ranges go to the work-groups so that each XCD holds a contiguous
+// block of them (a unit's contributors share an L2).  Units wholly inside a range are
 // finished in place; a unit cut by a range boundary leaves a partial
 // (O^T / l in bf16, running max and running sum l in fp32) in one of the
 // work-group's two workspace slots, and the combine kernel merges those
@@ -902,7 +903,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
     for (int k = threadIdx.x; k <= p.B; k += kThreads) p.ws_pre[k] = pre[k];
   const int total = pre[p.B];
   const int R = (total + p.G - 1) / p.G;
-  const int t_begin = blockIdx.x * R;
+  // Range index w of this work-group.  Work-group ids are dealt to the 8 XCDs
+  // round-robin, so XCD x = id % 8 takes a contiguous block of ranges: the
+  // contributors of a unit then share its Q (and any tiles they read close
+  // together in time) through that XCD's L2.
+  const int nx = p.G / 8, rx = p.G % 8, xcd = blockIdx.x % 8;
+  const int w = xcd * nx + min(xcd, rx) + (int)blockIdx.x / 8;
+  const int t_begin = w * R;
   const int t_end = min(t_begin + R, total);
   bool first = true;
   for (int t = t_begin; t < t_end;) {
@@ -911,7 +918,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
     const int i1 = min(t_end, u.start + u.T) - u.start;
     // slot 0 holds the partial of the range's first unit, slot 1 its last
     if (i0 < u.nreal)
-      run_unit<D, BIG>(p, u, i0, i1, i0 == 0 && i1 >= u.nreal, 2 * blockIdx.x + (first ? 0 : 1), ring,
+      run_unit<D, BIG>(p, u, i0, i1, i0 == 0 && i1 >= u.nreal, 2 * w + (first ? 0 : 1), ring,
                   pcache);
     first = false;
     t = u.start + i1;
