@@ -488,6 +488,8 @@ def main():
                     help="turn a rocprofv3 --stats kernel_stats.csv into a summary")
     ap.add_argument("--profile-command", default="",
                     help="command line recorded in a --summarize-* summary")
+    ap.add_argument("--only-block", type=int, default=0, choices=(0, 8, 32, 64),
+                    help="counter runs: the denoise layer's attention at this block size alone")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the config 2-4 attention entries and the oracle timings")
     args = ap.parse_args()
@@ -568,6 +570,48 @@ def main():
     def attn(s, i, stream=None):
         tt.tt_block_attn(desc, q[s][i], kb[s][i], vb[s][i], kp[i], vp[i], pt[i], ctx[i], out[i],
                          ws, stream)
+
+    def block_size_bench(S2):
+        """One attention launch per layer at block size S2 over the loop's
+        context pools, timed over 4 rounds of the layers (HIP events)."""
+        lens2 = p0.ctx_lens.astype(np.int64)
+        kvb = int(lens2.sum()) * lp.Hkv * lp.D * 2 * 2
+        stream2 = torch.cuda.current_stream()
+        d2 = tt.make_desc(B, S2, lp.Hq, lp.Hkv, lp.D, lp.page_size, p0.page_table.shape[1],
+                          p0.k_pages.shape[0], int(p0.ctx_lens.max()))
+        rng2 = np.random.Generator(np.random.PCG64(lp.seed * 100 + S2))
+        inp = [[dev_bf16(a) for a in workloads.block_inputs(rng2, B, S2, lp.Hq, lp.Hkv, lp.D)]
+               for _ in range(NL)]
+        o2 = torch.empty((B, S2, lp.Hq, lp.D), dtype=torch.bfloat16, device=dev)
+        ws2 = torch.empty(max(tt.tt_block_attn_workspace_bytes(d2), 16), dtype=torch.uint8,
+                          device=dev)
+        ctx.copy_(ctx0)
+        for i in range(NL):
+            tt.tt_block_attn(d2, *inp[i], kp[i], vp[i], pt[i], ctx[i], o2, ws2)
+        torch.cuda.synchronize()
+        n2 = 4 * NL
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream2)
+        for it in range(n2):
+            i = it % NL
+            tt.tt_block_attn(d2, *inp[i], kp[i], vp[i], pt[i], ctx[i], o2, ws2)
+        b1.record(stream2)
+        torch.cuda.synchronize()
+        t2 = b0.elapsed_time(b1) / 1e3 / n2
+        by2 = kvb + 2 * B * S2 * lp.Hq * lp.D * 2 + 2 * B * S2 * lp.Hkv * lp.D * 2
+        fl2 = 4 * lp.D * S2 * lp.Hq * int((lens2 + S2).sum())
+        log("block size %d: %.1f us/launch, %.0f GB/s, %.0f TFLOP/s" % (
+            S2, t2 * 1e6, by2 / t2 / 1e9, fl2 / t2 / 1e12))
+        return {"us_per_launch": t2 * 1e6, "GB/s": by2 / t2 / 1e9, "TFLOP/s": fl2 / t2 / 1e12,
+                "frac_hbm": by2 / t2 / 1e9 / HBM_PEAK_GBS,
+                "frac_mfma": fl2 / t2 / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                "query_chunks": -(-S2 * (lp.Hq // lp.Hkv) // 256)}
+
+    if args.only_block:
+        # counter runs: this block size's attention alone, then the calibration copy
+        block_size_bench(args.only_block)
+        calibration_copy(torch, dev)
+        return
 
     def one_block():
         ctx.copy_(ctx0)
@@ -685,37 +729,7 @@ def main():
     # 64 over the same context pools (the pages' block-size knob)
     block_sizes = None
     if extras:
-        block_sizes = {}
-        for S2 in (8, 32, 64):
-            d2 = tt.make_desc(B, S2, lp.Hq, lp.Hkv, lp.D, lp.page_size, p0.page_table.shape[1],
-                              p0.k_pages.shape[0], int(p0.ctx_lens.max()))
-            rng2 = np.random.Generator(np.random.PCG64(lp.seed * 100 + S2))
-            inp = [[dev_bf16(a) for a in workloads.block_inputs(rng2, B, S2, lp.Hq, lp.Hkv, lp.D)]
-                   for _ in range(NL)]
-            o2 = torch.empty((B, S2, lp.Hq, lp.D), dtype=torch.bfloat16, device=dev)
-            ws2 = torch.empty(max(tt.tt_block_attn_workspace_bytes(d2), 16), dtype=torch.uint8,
-                              device=dev)
-            for i in range(NL):
-                tt.tt_block_attn(d2, *inp[i], kp[i], vp[i], pt[i], ctx[i], o2, ws2)
-            torch.cuda.synchronize()
-            n2 = 4 * NL
-            a0.record(stream)
-            for it in range(n2):
-                i = it % NL
-                tt.tt_block_attn(d2, *inp[i], kp[i], vp[i], pt[i], ctx[i], o2, ws2)
-            a1.record(stream)
-            torch.cuda.synchronize()
-            t2 = a0.elapsed_time(a1) / 1e3 / n2
-            by2 = kv_bytes + 2 * B * S2 * lp.Hq * lp.D * 2 + 2 * B * S2 * lp.Hkv * lp.D * 2
-            fl2 = 4 * lp.D * S2 * lp.Hq * int((lens + S2).sum())
-            block_sizes[str(S2)] = {"us_per_launch": t2 * 1e6, "GB/s": by2 / t2 / 1e9,
-                                    "TFLOP/s": fl2 / t2 / 1e12,
-                                    "frac_hbm": by2 / t2 / 1e9 / HBM_PEAK_GBS,
-                                    "frac_mfma": fl2 / t2 / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                                    "context_passes": -(-S2 * (lp.Hq // lp.Hkv) // 256)}
-            log("block size %d: %.1f us/launch, %.0f GB/s, %.0f TFLOP/s" % (
-                S2, t2 * 1e6, by2 / t2 / 1e9, fl2 / t2 / 1e12))
-            del inp, o2, ws2
+        block_sizes = {str(S2): block_size_bench(S2) for S2 in (8, 32, 64)}
 
     # ---- unmask alone (flags 0: the all-masked state is left untouched)
     mask.copy_(ones)

@@ -8,12 +8,16 @@
 // S block tokens], softmax over all of them, no mask.
 //
 // Work decomposition.  A *unit* is (sequence b, KV head h, query chunk of up
-// to 256 rows).  A unit's keys are cut into 64-token *tiles*: ceil(L_b/64)
-// context tiles, one tile holding the S block tokens, then kUnitPad virtual
-// tiles that only stand for the unit's fixed cost.  All tiles of all units
-// form one flat list; range w of G is [w*R, (w+1)*R), R = ceil(total/G),
-// and the ranges go to the work-groups so that each XCD holds a contiguous
-// block of them (a unit's contributors share an L2).  Units wholly inside a range are
+// to 256 rows).  The keys of a (b, h) pair are cut into 64-token *tiles*:
+// ceil(L_b/64) context tiles, one tile holding the S block tokens, then
+// kUnitPad virtual tiles that only stand for a unit's fixed cost.  The tiles
+// of all (b, h) pairs form one flat list.  The G work-groups form G/Q teams
+// of Q = (query chunks per pair) members; team k takes the range [k*R,
+// (k+1)*R), R = ceil(total/(G/Q)), and member m computes query chunk m over
+// it, so the Q chunks of a pair stream the same context tiles side by side.
+// Ranges go to the work-groups so that each XCD holds a contiguous block of
+// them: a team, and the teams that share a unit, then share an L2, and the
+// context of a pair is fetched from HBM about once.  Units wholly inside a range are
 // finished in place; a unit cut by a range boundary leaves a partial
 // (O^T / l in bf16, running max and running sum l in fp32) in one of the
 // work-group's two workspace slots, and the combine kernel merges those
@@ -91,12 +95,12 @@ struct Params {
 __device__ __forceinline__ int real_tiles(int L) { return (L + kTile - 1) / kTile + 1; }
 __device__ __forceinline__ int seq_tiles(int L) { return real_tiles(L) + kUnitPad; }
 
-// pre[b] = first flat tile of sequence b (all its units), pre[B] = total;
+// pre[b] = first flat tile of sequence b (all its KV heads), pre[B] = total;
 // lens[b] = clamped context length.  One wave scans 64 sequences per step.
 __device__ void build_prefix(const Params &p, int *pre, int *lens) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const int upb = p.Hkv * p.qchunks;
+    const int upb = p.Hkv;  // one tile run per (b, h); its query chunks share it
     int carry = 0;
     for (int base = 0; base < p.B; base += 64) {
       const int b = base + lane;
@@ -123,8 +127,8 @@ struct Unit {
   int b, h, qc, L, T, nreal, start, id;
 };
 
-// The unit that owns flat tile t.
-__device__ Unit locate(const Params &p, const int *pre, const int *lens, int t) {
+// The unit of query chunk qc that owns flat tile t.
+__device__ Unit locate(const Params &p, const int *pre, const int *lens, int t, int qc) {
   int lo = 0, hi = p.B;  // pre[lo] <= t < pre[hi]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -135,11 +139,11 @@ __device__ Unit locate(const Params &p, const int *pre, const int *lens, int t) 
   u.L = lens[lo];
   u.T = seq_tiles(u.L);
   u.nreal = real_tiles(u.L);
-  const int ui = (t - pre[lo]) / u.T;
-  u.h = ui / p.qchunks;
-  u.qc = ui % p.qchunks;
-  u.start = pre[lo] + ui * u.T;
-  u.id = lo * p.Hkv * p.qchunks + ui;
+  const int h = (t - pre[lo]) / u.T;
+  u.h = h;
+  u.qc = qc;
+  u.start = pre[lo] + h * u.T;
+  u.id = (lo * p.Hkv + h) * p.qchunks + qc;
   return u;
 }
 
@@ -902,18 +906,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
   if (blockIdx.x == 0)
     for (int k = threadIdx.x; k <= p.B; k += kThreads) p.ws_pre[k] = pre[k];
   const int total = pre[p.B];
-  const int R = (total + p.G - 1) / p.G;
-  // Range index w of this work-group.  Work-group ids are dealt to the 8 XCDs
-  // round-robin, so XCD x = id % 8 takes a contiguous block of ranges: the
-  // contributors of a unit then share its Q (and any tiles they read close
-  // together in time) through that XCD's L2.
+  const int teams = p.G / p.qchunks;
+  const int R = (total + teams - 1) / teams;
+  // Index w of this work-group in range order.  Work-group ids are dealt to
+  // the 8 XCDs round-robin, so XCD x = id % 8 takes a contiguous block of
+  // indices: the members of a team, and the contributors of a unit, then
+  // share its tiles and its Q through that XCD's L2.
   const int nx = p.G / 8, rx = p.G % 8, xcd = blockIdx.x % 8;
   const int w = xcd * nx + min(xcd, rx) + (int)blockIdx.x / 8;
-  const int t_begin = w * R;
+  const int qc = w % p.qchunks;
+  const int t_begin = (w / p.qchunks) * R;
   const int t_end = min(t_begin + R, total);
   bool first = true;
   for (int t = t_begin; t < t_end;) {
-    const Unit u = locate(p, pre, lens, t);
+    const Unit u = locate(p, pre, lens, t, qc);
     const int i0 = t - u.start;
     const int i1 = min(t_end, u.start + u.T) - u.start;
     // slot 0 holds the partial of the range's first unit, slot 1 its last
@@ -928,11 +934,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_split_kernel(Params p) {
 // Merges the partials of units cut by a range boundary:
 //   O = sum_w c_w (O_w / l_w) / sum_w c_w,  c_w = 2^(m_w - M) l_w,  M = max_w m_w.
 // Work-group per (unit, 16-feature slice, 64-row chunk): lane = query row,
-// and the contributors (the work-groups whose ranges meet the unit's real
-// tiles, w_lo .. w_hi) are dealt round-robin to the waves, each keeping an
-// online (max, sum, O) over its share; the waves' states are then merged
-// through LDS.  Contributor w left its partial in slot 2w, or 2w + 1 for w_lo
-// when its range began inside an earlier unit.
+// and the contributors (the teams whose ranges meet the unit's real tiles,
+// w_lo .. w_hi; of each, the member of the unit's query chunk) are dealt
+// round-robin to the waves, each keeping an online (max, sum, O) over its
+// share; the waves' states are then merged through LDS.  The member of team
+// k for chunk qc is work-group index i = k * qchunks + qc; it left its partial
+// in slot 2i, or 2i + 1 for team w_lo when its range began inside an earlier
+// (b, h) pair.
 constexpr int kCombineRows = 64;
 constexpr int kCombineFeat = 16;
 constexpr int kCombineWaves = 4;
@@ -945,19 +953,22 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_combine_kernel(Params
   const int b = uid / upb, ui = uid % upb;
   const int h = ui / p.qchunks, qc = ui % p.qchunks;
   const int pb = p.ws_pre[b];
-  const int T = (p.ws_pre[b + 1] - pb) / upb;
+  const int T = (p.ws_pre[b + 1] - pb) / p.Hkv;
   const int total = p.ws_pre[p.B];
   const int nreal = T - kUnitPad;
-  const int us = pb + ui * T;
-  const int R = (total + p.G - 1) / p.G;
+  const int us = pb + h * T;
+  const int teams = p.G / p.qchunks;
+  const int R = (total + teams - 1) / teams;
+  // contributing teams; team k's member for query chunk qc is work-group
+  // index k * qchunks + qc
   const int w_lo = us / R, w_hi = (us + nreal - 1) / R;
   if (w_lo == w_hi) return;  // finished in place by one work-group
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qloc = blockIdx.z * kCombineRows + lane;
   const int qi = qc * kQRows + qloc;
   const bool row_ok = qi < p.S * p.g;
-  const int lo_slot = 2 * w_lo + (w_lo * R != us ? 1 : 0);
-  auto slot_of = [&](int w) { return w == w_lo ? lo_slot : 2 * w; };
+  const int lo_slot = 2 * (w_lo * p.qchunks + qc) + (w_lo * R != us ? 1 : 0);
+  auto slot_of = [&](int w) { return w == w_lo ? lo_slot : 2 * (w * p.qchunks + qc); };
 
   // features f0 .. f0+15 of this row: 16-byte pieces at accumulator block
   // db = f0/32, register groups r4 = (f0%32)/8 + {0, 1}, lane halves hh = 0, 1
@@ -1086,7 +1097,10 @@ AttnPlan plan_bf16_attn(const tt_attn_desc &d, int cus) {
   long long G = (tiles + kMinTiles - 1) / kMinTiles;
   if (G > cus) G = cus;
   if (G > 1024) G = 1024;  // the combine keeps one slot id per contributor in LDS
-  if (G < 1) G = 1;
+  // whole teams of qchunks work-groups (qchunks <= 1024: S <= 64 rows times
+  // at most 4096 query heads over 256-row chunks)
+  G = G / p.qchunks * p.qchunks;
+  if (G < p.qchunks) G = p.qchunks;
   p.G = (int)G;
   p.ws_bytes = ws_pre_bytes(p.B) + (size_t)2 * G * ((size_t)p.D * kQRows * 2 + 2 * kQRows * sizeof(float));
   return p;
