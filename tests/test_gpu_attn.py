@@ -82,6 +82,14 @@ EDGE = [
     ("lag_partly_idle", 2, 10, 32, 2, 128, [100, 3000], 256),
     # S*g = 384: the second query chunk holds 128 rows, its waves 4-7 are idle
     ("second_chunk_half_full", 2, 24, 32, 2, 128, [90, 2000], 256),
+    # S*g = 768: teams of 3 work-groups (the work-group count is a multiple of
+    # 3, not of 8), ranges long enough that teams cut pairs
+    ("three_chunk_teams", 3, 48, 32, 2, 128, [1500, 6000, 300], 256),
+    # S*g = 4096: teams of 16 larger than the range count a tiny context
+    # needs, so one team covers every tile
+    ("one_team_16_chunks", 1, 64, 64, 1, 64, [100], 64),
+    # S*g = 16384: teams of 64 chunks over a longer context
+    ("teams_of_64_chunks", 1, 64, 256, 1, 128, [2000], 256),
 ]
 
 
