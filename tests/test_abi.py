@@ -127,6 +127,31 @@ def test_workspace_sizes(lib):
     assert n.value >= 32 * 16 * 16
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv,max_ctx,chunks", [
+    (32, 16, 32, 2, 8192, 1), (32, 32, 32, 2, 8192, 2), (32, 48, 32, 2, 8192, 3),
+    (32, 64, 32, 2, 8192, 4),
+    (1, 64, 64, 1, 100, 16),  # 7 tiles would give 2 work-groups: one team of 16 instead
+])
+def test_plan_uses_whole_query_chunk_teams(lib, B, S, Hq, Hkv, max_ctx, chunks):
+    """The bf16 plan forms teams of one work-group per 256-row query chunk of a
+    (sequence, KV head) pair, so its work-group count G is a whole number of
+    teams (at least one), at most the 256 CUs planned for without a device.
+    G is read back from the workspace size: the published prefix, then two
+    partial slots per work-group (bf16 O of 256 rows x D, fp32 max and sum)."""
+    D = 128
+    d = good_desc(B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, max_ctx_len=max_ctx, page_size=256,
+                  max_pages=(max_ctx + 255) // 256, num_pages=B * ((max_ctx + 255) // 256))
+    n = ctypes.c_size_t(0)
+    assert lib.tt_block_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    pre = ((B + 1) * 4 + 255) // 256 * 256
+    slot = D * 256 * 2 + 256 * 2 * 4
+    assert (n.value - pre) % (2 * slot) == 0
+    G = (n.value - pre) // (2 * slot)
+    assert G % chunks == 0 and chunks <= G <= max(256, chunks)
+    if B == 1:
+        assert G == chunks
+
+
 def test_tile_count_beyond_device_index(lib):
     """The device plans with int tile indices: a shape whose flat tile list
     could exceed that range is rejected on the host (TT_ERR_SHAPE) by both the
