@@ -130,7 +130,7 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("B,S,Hq,Hkv,max_ctx,chunks", [
     (32, 16, 32, 2, 8192, 1), (32, 32, 32, 2, 8192, 2), (32, 48, 32, 2, 8192, 3),
     (32, 64, 32, 2, 8192, 4),
-    (1, 64, 64, 1, 100, 16),  # 7 tiles would give 2 work-groups: one team of 16 instead
+    (1, 64, 64, 1, 100, 16),  # a short context: 28 work-groups round down to one team of 16
 ])
 def test_plan_uses_whole_query_chunk_teams(lib, B, S, Hq, Hkv, max_ctx, chunks):
     """The bf16 plan forms teams of one work-group per 256-row query chunk of a
