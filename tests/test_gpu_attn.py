@@ -90,6 +90,8 @@ EDGE = [
     ("one_team_16_chunks", 1, 64, 64, 1, 64, [100], 64),
     # S*g = 16384: teams of 64 chunks over a longer context
     ("teams_of_64_chunks", 1, 64, 256, 1, 128, [2000], 256),
+    # two chunks per pair with 16-token pages (per-lane page lookups)
+    ("two_chunks_small_pages", 2, 32, 32, 2, 128, [100, 900], 16),
 ]
 
 
