@@ -101,6 +101,16 @@ def test_edge_cases(name, B, S, Hq, Hkv, D, lens, ps):
     _run_full(c, name)
 
 
+def test_maximum_batch():
+    """The largest batch the ABI accepts (2048 sequences): the device prefix
+    scans 32 groups of 64 lengths, and each work-group's range spans many short
+    units (lengths 0..299, some empty), compared whole-tensor and per unit."""
+    lens = [int(x) for x in np.random.Generator(np.random.PCG64(2048)).integers(0, 300, 2048)]
+    lens[:3] = [0, 0, 299]
+    c = _case(2048, 2048, 1, 4, 2, 64, lens, 16)
+    _run_full(c, "maximum batch")
+
+
 def test_fp32_edge_cases():
     for seed, (B, S, Hq, Hkv, D, lens, ps) in enumerate([
             (2, 16, 4, 1, 64, [0, 48], 16), (2, 1, 8, 2, 128, [300, 1], 32),

@@ -78,6 +78,22 @@ def test_kv_append_unaligned_block(which):
     assert np.array_equal(_bits(dc.v_pages, "bf16").view(np.uint8), vp.view(np.uint8))
 
 
+def test_kv_append_maximum_batch():
+    """Bit-exact append for the largest batch the ABI accepts (2048 sequences,
+    one work-group each), lengths 0..299 with 16-token pages."""
+    import two_tower_attention_amd as tt
+    rng = np.random.Generator(np.random.PCG64(2049))
+    lens = [int(x) for x in rng.integers(0, 300, 2048)]
+    c = workloads.make_attn_case(rng, B=2048, S=4, Hq=2, Hkv=2, D=64, ctx_lens=lens,
+                                 page_size=16, extra_tokens=4)
+    dc = DevCase(c)
+    tt.tt_kv_append(dc.desc, dc.k_blk, dc.v_blk, dc.k_pages, dc.v_pages, dc.page_table, dc.ctx_lens)
+    kp, vp, nl = oracle.kv_append(c.k_pages, c.v_pages, c.page_table, c.ctx_lens, c.k_blk, c.v_blk)
+    assert np.array_equal(dc.ctx_lens.cpu().numpy(), nl)
+    assert np.array_equal(_bits(dc.k_pages, "bf16").view(np.uint8), kp.view(np.uint8))
+    assert np.array_equal(_bits(dc.v_pages, "bf16").view(np.uint8), vp.view(np.uint8))
+
+
 def test_kv_append_skips_sequence_without_pages():
     import two_tower_attention_amd as tt
     rng = np.random.Generator(np.random.PCG64(3))
