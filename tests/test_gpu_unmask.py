@@ -58,6 +58,18 @@ def test_config5_unmask_full_size():
         check(logits, mask, None, rem)
 
 
+@pytest.mark.parametrize("B,S", [(4095, 16), (65535, 1)])
+def test_maximum_rows(B, S):
+    """The most rows the ABI accepts (batch * block <= 65535; one row per
+    work-group column), an odd vocabulary, a random mask and k from
+    remaining_steps."""
+    rng = np.random.Generator(np.random.PCG64(B + S))
+    V = 257
+    logits = workloads.make_logits(rng, B * S, V)
+    mask = (rng.random((B, S)) < 0.6).astype(np.uint8)
+    check(logits, mask, None, 2)
+
+
 @pytest.mark.parametrize("V", [1, 3, 1000, 1023, 4097, 40000])
 def test_odd_vocab_sizes(V):
     rng = np.random.Generator(np.random.PCG64(V))
