@@ -92,6 +92,10 @@ EDGE = [
     ("teams_of_64_chunks", 1, 64, 256, 1, 128, [2000], 256),
     # two chunks per pair with 16-token pages (per-lane page lookups)
     ("two_chunks_small_pages", 2, 32, 32, 2, 128, [100, 900], 16),
+    # the largest page size: a tile's keys and values inside one 4096-token page
+    ("pages_4096", 2, 16, 32, 2, 128, [5000, 100], 4096),
+    # the most heads: 4096 one-row units (S*g = 1), seven of eight waves idle
+    ("max_heads_mha", 1, 1, 4096, 4096, 64, [10], 16),
 ]
 
 
