@@ -54,10 +54,10 @@ constexpr int kThreads = 64 * (kQRows / 32);  // one wave per 32 query rows
 constexpr int kStages = TT_ATTN_STAGES;  // LDS ring depth (tiles in flight + 1)
 constexpr int kPageCache = 1024; // page ids cached per sub-range
 constexpr int kMinTiles = 4;     // smallest range worth a work-group
-// Each unit carries kUnitPad virtual tiles after its real ones: they stand
-// for the unit's fixed cost (Q load, page-id cache, pipeline fill, block
-// tile, epilogue) so that ranges which cut unit boundaries get fewer real
-// tiles.  A virtual tile holds no work.
+// Each (sequence, KV head) tile run carries kUnitPad virtual tiles after its
+// real ones: they stand for a unit's fixed cost (Q load, page-id cache,
+// pipeline fill, block tile, epilogue) so that ranges which cut run
+// boundaries get fewer real tiles.  A virtual tile holds no work.
 #ifndef TT_ATTN_UNITPAD
 #define TT_ATTN_UNITPAD 4
 #endif
@@ -91,7 +91,7 @@ struct Params {
   float sl2;
 };
 
-// real tiles of a unit: context tiles plus the block tile
+// real tiles of a (sequence, KV head) run: context tiles plus the block tile
 __device__ __forceinline__ int real_tiles(int L) { return (L + kTile - 1) / kTile + 1; }
 __device__ __forceinline__ int seq_tiles(int L) { return real_tiles(L) + kUnitPad; }
 
